@@ -1,0 +1,89 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module holds no attention arithmetic: it only draws random numbers, applies
+the planted-row structure and rounds to the storage dtype.  Both the HIP path
+(tests, benchmark) and the CPU oracle receive the arrays it returns, so the oracle
+sees exactly the values the GPU sees.
+
+Recipe (shared by every workload):
+  rng = numpy.random.default_rng(seed); draw Q, K, V, dO in that order, each
+  ``rng.standard_normal((B, H, N, d), dtype=float32)`` in C order; optionally scale
+  one query row by a constant (the planted row) before rounding; round to bf16 with
+  round-to-nearest-even (torch CPU ``.to(torch.bfloat16)``) unless the workload is
+  fp32.  The softmax scale is 1/sqrt(d).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "to_f64"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str  # "bf16" or "fp32"
+    backward: bool
+    planted: tuple | None = None  # (b, h, row, factor) applied to Q before rounding
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    def with_(self, **kw) -> "Workload":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return Workload(**d)
+
+
+# The five workloads: shapes, masks and dtypes as the attention layers they stand in for.
+WORKLOADS = {
+    "tiny_fp32": Workload("tiny_fp32", 1, 1, 256, 64, False, "fp32", True),
+    "gpt2m_fwd": Workload("gpt2m_fwd", 8, 16, 1024, 64, False, "bf16", False),
+    "long_causal": Workload("long_causal", 4, 32, 4096, 128, True, "bf16", True,
+                            planted=(0, 0, 2049, 30.0)),
+    "train_step": Workload("train_step", 4, 16, 2048, 64, True, "bf16", True),
+    "long_context": Workload("long_context", 1, 16, 16384, 128, True, "bf16", True),
+}
+
+
+def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if dtype == "bf16":
+        return t.to(torch.bfloat16)
+    if dtype == "fp32":
+        return t.to(torch.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def make_inputs(w: Workload, with_do: bool | None = None) -> dict:
+    """Draw the workload's tensors. Returns dict q, k, v[, do] of CPU torch tensors."""
+    if with_do is None:
+        with_do = w.backward
+    rng = np.random.default_rng(w.seed)
+    shape = (w.B, w.H, w.N, w.d)
+    names = ["q", "k", "v"] + (["do"] if with_do else [])
+    out = {}
+    for name in names:
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if name == "q" and w.planted is not None:
+            b, h, row, factor = w.planted
+            if b < w.B and h < w.H and row < w.N:
+                x[b, h, row, :] *= np.float32(factor)
+        out[name] = _round(x, w.dtype)
+    return out
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact float64 copy of a bf16/fp32 CPU tensor."""
+    return t.detach().to("cpu").to(torch.float64).numpy()

@@ -1,0 +1,76 @@
+"""Host-side FLOP / byte / tile accounting against the numbers the pages print.
+
+Sources: "FlashAttention and online softmax" (ML Systems Lesson 4), sections
+"HBM traffic", "Backward pass: recompute instead of store", "Causal masks and
+FlashAttention-3", "4. Worked example (c) At scale" and "5. In code".
+"""
+import math
+
+import numpy as np
+import torch
+
+from exact_io_aware_14_amd import accounting as acc
+
+
+def _sig(x, n):
+    return float(f"{x:.{n}g}")
+
+
+def test_causal_tile_count(golden):
+    g = golden("accounting.json")["causal_tiles"]
+    computed, total = acc.causal_tiles(g["N"], g["B"])
+    assert (computed, total) == (g["computed"], g["total"])
+    # brute force: a tile (i, j) is computed unless it lies wholly above the diagonal
+    T = g["N"] // g["B"]
+    brute = sum(1 for i in range(T) for j in range(T) if j * g["B"] <= i * g["B"] + g["B"] - 1)
+    assert brute == computed
+
+
+def test_at_scale_numbers(golden):
+    g = golden("accounting.json")["at_scale"]
+    N, d, Br = g["N"], g["d"], g["Br"]
+    assert N * N * 2 == g["S_bytes_per_head_bf16"]
+    assert g["heads"] * N * 4 == g["lse_bytes_all_heads"]
+    n = g["printed_sig_digits"]
+    assert _sig(acc.fwd_flops(1, 1, N, d, False), n) == g["flops_per_head"]
+    assert _sig(acc.standard_traffic_elems(N, d), n) == g["standard_elems"]
+    assert _sig(acc.flash_traffic_elems(N, d, Br), n) == g["flash_elems_Br128"]
+    # the ratio for N >> d is 2 Br / d
+    ratio = acc.standard_traffic_elems(N, d) / acc.flash_traffic_elems(N, d, Br)
+    assert abs(ratio - 2 * Br / d) < 0.05
+
+
+def test_flop_convention(golden):
+    f = golden("accounting.json")["flop_factors"]
+    B, H, N, d = 2, 3, 128, 64
+    assert acc.fwd_flops(B, H, N, d, False) == f["forward"] * B * H * N * N * d
+    assert acc.bwd_flops(B, H, N, d, False) == f["flash_backward"] * B * H * N * N * d
+    assert acc.fwd_flops(B, H, N, d, True) == acc.fwd_flops(B, H, N, d, False) / 2
+    assert acc.bwd_flops(B, H, N, d, True) == 2.5 * acc.fwd_flops(B, H, N, d, True)
+
+
+def test_naive_saved_bytes(golden):
+    """The naive autograd graph keeps Q, K, V and the N x N P (section 5 listing)."""
+    g = golden("accounting.json")["saved_bytes"]
+    N, d = g["N"], g["d"]
+    torch.manual_seed(0)
+    x = [torch.randn(1, 1, N, d, dtype=torch.float32, requires_grad=True) for _ in range(3)]
+    seen = {}
+
+    def pack(t):
+        seen[t.untyped_storage().data_ptr()] = t.untyped_storage().nbytes()
+        return t
+
+    with torch.autograd.graph.saved_tensors_hooks(pack, lambda t: t):
+        torch.softmax(x[0] @ x[1].transpose(-1, -2) / math.sqrt(d), dim=-1) @ x[2]
+    assert sum(seen.values()) == g["naive"] == g["naive_qkv"] + g["naive_p"]
+    # what the fused method keeps: Q, K, V, O in the input dtype plus one fp32 lse per row
+    fused = 4 * N * d * g["bytes_per_elem"] + 4 * N
+    assert fused == g["fused"] == g["fused_qkvo"] + g["fused_lse"]
+
+
+def test_byte_model():
+    B, H, N, d = 4, 32, 4096, 128
+    assert acc.fwd_bytes(B, H, N, d, "bf16") == 4 * B * H * N * d * 2 + 4 * B * H * N
+    mib = acc.fwd_bytes(B, H, N, d, "bf16") / 2**20
+    assert 513 < mib < 515  # Q, K, V, O at 128 MiB each plus 2 MiB of lse

@@ -1,0 +1,321 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test names the passage it follows.  Pages: "FlashAttention and online
+softmax" (ML Systems Lesson 4) is the main source.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+from oracle import (attention_bwd, attention_fwd, merge, online_softmax,
+                    three_pass_softmax_average, tiled_forward)
+
+
+def _one_query(scores, values):
+    """Shape scores/values as one query of a d=1 head with scale 1: S_0j = scores_j."""
+    n = len(scores)
+    Q = np.ones((1, 1, n, 1))  # every query row has the same q = 1
+    K = np.asarray(scores, dtype=np.float64).reshape(1, 1, n, 1)
+    V = np.asarray(values, dtype=np.float64).reshape(1, 1, n, 1)
+    return Q, K, V
+
+
+# --- worked examples printed on the pages ------------------------------------------
+
+def test_small_numbers_online(golden):
+    """Lesson 4, "One query, one pass", 'Small numbers': (1,2) then 4 gives l=1.185."""
+    g = golden("online_softmax_small_numbers.json")
+    r = online_softmax([1.0, 2.0, 4.0], block=2, trace=True)
+    (m1, f1, l1, _), (m2, f2, l2, _) = r["steps"]
+    dec = g["printed_decimals"]
+    assert m1 == g["after_block_1"]["m"] and round(l1, dec) == g["after_block_1"]["l"]
+    b2 = g["after_block_2"]
+    assert m2 == b2["m"]
+    assert round(f2, dec) == b2["factor"]
+    assert round(f2 * l1, dec) == b2["rescaled_old_sum"]
+    assert round(l2, dec) == b2["l"]
+    # exact forms behind the printed decimals
+    assert l1 == pytest.approx(1 + math.exp(-1), rel=1e-15)
+    assert l2 == pytest.approx(math.exp(-3) + math.exp(-2) + 1, rel=1e-15)
+
+
+def test_small_numbers_oracle_lse(golden):
+    """The naive oracle's lse for scores (1, 2, 4) equals m + log l of the same example."""
+    g = golden("online_softmax_small_numbers.json")
+    Q, K, V = _one_query([1.0, 2.0, 4.0], [0.0, 0.0, 0.0])
+    _, lse = attention_fwd(Q, K, V, scale=1.0)
+    assert round(math.exp(lse[0, 0, 0] - 4.0), 3) == g["after_block_2"]["l"]
+
+
+def test_worked_example_a(golden):
+    """Lesson 4, section 4 (a): factors 0 then 1/4, l 1.5 then 1.875, o~ 2 then 5.5."""
+    g = golden("worked_example_a.json")
+    x = np.log(g["x_exp"])
+    r = online_softmax(x, g["v"], block=g["block"], trace=True)
+    for (m, f, l, o), want in zip(r["steps"], g["steps"]):
+        assert math.exp(m) == pytest.approx(want["m_exp"], rel=1e-15)
+        assert f == pytest.approx(want["factor"], abs=1e-15)
+        assert l == pytest.approx(want["l"], rel=1e-15)
+        assert o == pytest.approx(want["o_tilde"], rel=1e-15)
+    exact = g["output_num"] / g["output_den"]
+    assert r["o"] == pytest.approx(exact, rel=1e-15)
+    assert r["lse"] == pytest.approx(math.log(g["lse_exp"]), rel=1e-15)
+
+
+def test_worked_example_a_oracle(golden):
+    """The naive oracle reaches the same 44/15 and ln 15 (direct check of part (a))."""
+    g = golden("worked_example_a.json")
+    Q, K, V = _one_query(np.log(g["x_exp"]), g["v"])
+    O, lse = attention_fwd(Q, K, V, scale=1.0)
+    assert O[0, 0, 0, 0] == pytest.approx(g["output_num"] / g["output_den"], rel=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(math.log(g["lse_exp"]), rel=1e-15)
+
+
+def test_check_yourself_1(golden):
+    """Lesson 4, section 8, question 1: continuing from (m, l, o~) = (3, 2, 5)."""
+    g = golden("check_yourself_1.json")
+    st = g["state"]
+    r = online_softmax(g["block_scores"], g["block_values"], block=2,
+                       state=(st["m"], st["l"], st["o_tilde"]), trace=True)
+    m, f, l, o = r["steps"][0]
+    e, dec = g["expect"], g["printed_decimals"]
+    assert m == e["m"]
+    assert round(f, dec) == e["factor"]
+    assert round(l, dec) == e["l"] and l == pytest.approx(1 + 3 * math.exp(-2), rel=1e-15)
+    assert round(o, dec) == e["o_tilde"] and o == pytest.approx(1 + 5 * math.exp(-2), rel=1e-15)
+    assert round(o / l, dec) == e["output"]
+
+
+def test_merge_examples(golden):
+    """Lesson 4, section 4 (b), section 8 question 2 and the merge quick check."""
+    for c in golden("merges.json")["cases"]:
+        o, lse = merge(c["o_a_num"] / c["o_a_den"], math.log(c["lse_a_exp"]),
+                       c["o_b_num"] / c["o_b_den"], math.log(c["lse_b_exp"]))
+        assert float(o) == pytest.approx(c["o_num"] / c["o_den"], rel=1e-15)
+        assert float(lse) == pytest.approx(math.log(c["lse_exp"]), rel=1e-15)
+        if "wrong_plain_average" in c:
+            assert abs(float(o) - c["wrong_plain_average"]) > 0.5
+            wa = math.exp(math.log(c["lse_a_exp"]) - float(lse))
+            assert wa == pytest.approx(c["w_a"], rel=1e-15)
+            assert 1 - wa == pytest.approx(c["w_b"], rel=1e-15)
+
+
+def test_merge_empty_sets():
+    """Merging with an empty set: weight 0; both empty: o = 0, lse = -inf, no NaN."""
+    o, lse = merge(np.array([[1.0, 2.0]]), np.array([-np.inf]),
+                   np.array([[3.0, 4.0]]), np.array([0.5]))
+    assert np.array_equal(o, [[3.0, 4.0]]) and lse[0] == 0.5
+    o, lse = merge(np.zeros((2, 3)), np.full(2, -np.inf), np.zeros((2, 3)), np.full(2, -np.inf))
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+def test_merge_of_oracle_partials():
+    """Attention over keys A and B separately, merged by lse, equals the oracle over A u B."""
+    rng = np.random.default_rng(3)
+    N, d = 40, 8
+    Q, K, V = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    split = np.zeros((N, N), dtype=bool)
+    split[:, :17] = True
+    oa, la = attention_fwd(Q, K, V, 0.3, mask=split)
+    ob, lb = attention_fwd(Q, K, V, 0.3, mask=~split)
+    o, lse = merge(oa, la, ob, lb)
+    O, L = attention_fwd(Q, K, V, 0.3)
+    assert np.abs(o - O).max() < 1e-14 and np.abs(lse - L).max() < 1e-13
+
+
+# --- invariants and closed forms -------------------------------------------------------
+
+@pytest.mark.parametrize("block", [1, 7, 16, 128, 1000])
+def test_online_equals_three_pass(block):
+    """Lesson 4, 'One query, one pass' figure text: online and exact differ ~1e-16."""
+    rng = np.random.default_rng(block)
+    worst = 0.0
+    for _ in range(20):
+        x = rng.standard_normal(1000) * 3.0
+        v = rng.standard_normal((1000, 4))
+        ref = three_pass_softmax_average(x, v)
+        got = online_softmax(x, v, block=block)["o"]
+        worst = max(worst, float(np.abs(got - ref).max() / np.abs(ref).max()))
+    assert worst < 1e-14
+
+
+def test_rows_of_p_sum_to_one():
+    """Each row of P sums to one: with V = 1 the output is exactly 1 (up to rounding)."""
+    rng = np.random.default_rng(1)
+    N, d = 300, 16
+    Q, K = (rng.standard_normal((2, 1, N, d)) for _ in range(2))
+    ones = np.ones((2, 1, N, d))
+    for causal in (False, True):
+        O, _ = attention_fwd(Q, K, ones, 0.25, causal=causal, row_block=64)
+        assert np.abs(O - 1).max() < 1e-14
+
+
+def test_huge_scores_do_not_overflow():
+    """Lesson 4, 'One query, one pass': subtracting the max stops exp overflowing;
+    theorem proof step 5: every exponent <= 0."""
+    x = np.array([800.0, 1e4, 0.0, -5.0, 1e4 - 1.0])
+    with np.errstate(over="ignore"):
+        assert not np.isfinite(np.exp(x).sum())  # the naive form overflows
+    Q, K, V = _one_query(x, [1.0, 2.0, 3.0, 4.0, 5.0])
+    O, lse = attention_fwd(Q, K, V, scale=1.0)
+    assert np.isfinite(O).all() and np.isfinite(lse).all()
+    w = np.array([0.0, 1.0, 0.0, 0.0, math.exp(-1.0)])
+    assert O[0, 0, 0, 0] == pytest.approx((2 * w[1] + 5 * w[4]) / w.sum(), rel=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(1e4 + math.log1p(math.exp(-1.0)), rel=1e-15)
+    r = online_softmax(x, [1.0, 2.0, 3.0, 4.0, 5.0], block=2)
+    assert r["o"] == pytest.approx(O[0, 0, 0, 0], rel=1e-15)
+
+
+def test_fully_masked_rows():
+    """Lesson 4, 'Merging two partial results' and 'Common mistakes': a row with no
+    visible key gives o = 0 and lse = -inf, and no NaN reaches the gradients."""
+    rng = np.random.default_rng(5)
+    N, d = 6, 3
+    Q, K, V, dO = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    mask = np.ones((N, N), dtype=bool)
+    mask[2] = False
+    O, lse = attention_fwd(Q, K, V, 0.5, mask=mask)
+    assert np.all(O[0, 0, 2] == 0) and lse[0, 0, 2] == -np.inf
+    assert np.isfinite(O).all() and np.isfinite(np.delete(lse, 2, axis=2)).all()
+    dQ, dK, dV = attention_bwd(Q, K, V, dO, 0.5, mask=mask)
+    assert np.isfinite(dQ).all() and np.isfinite(dK).all() and np.isfinite(dV).all()
+    assert np.all(dQ[0, 0, 2] == 0)
+
+
+def test_causal_convention():
+    """Causal: query i sees keys j <= i (lower triangle incl. diagonal)."""
+    rng = np.random.default_rng(2)
+    N, d = 9, 4
+    Q, K, V = (rng.standard_normal((1, 1, N, d)) for _ in range(3))
+    O, lse = attention_fwd(Q, K, V, 0.5, causal=True)
+    for i in range(N):
+        # row i over keys 0..i only, as a non-causal query against the first i+1 keys
+        Qi = np.repeat(Q[:, :, i:i + 1], i + 1, axis=2)
+        Or, lr = attention_fwd(Qi, K[:, :, :i + 1], V[:, :, :i + 1], 0.5)
+        assert np.abs(O[0, 0, i] - Or[0, 0, 0]).max() < 1e-15
+        assert abs(lse[0, 0, i] - lr[0, 0, 0]) < 1e-14
+    assert O[0, 0, 0] == pytest.approx(V[0, 0, 0], rel=1e-15)  # first row sees only key 0
+
+
+def test_lse_is_scipy_logsumexp():
+    """lse is the natural-log logsumexp of the scaled score row (the 'In code' listing
+    computes it with scipy's logsumexp)."""
+    rng = np.random.default_rng(4)
+    N, d = 130, 8
+    Q, K, V = (rng.standard_normal((1, 2, N, d)) for _ in range(3))
+    for causal in (False, True):
+        _, lse = attention_fwd(Q, K, V, 0.7, causal=causal, row_block=50)
+        for h in range(2):
+            S = 0.7 * Q[0, h] @ K[0, h].T
+            if causal:
+                S = np.where(np.tri(N, dtype=bool), S, -np.inf)
+            assert np.abs(lse[0, h] - logsumexp(S, axis=1)).max() < 1e-13
+
+
+def test_tiled_equals_naive():
+    """Lesson 4, section 5 'In code' (b): tiled forward = naive at N=100, d=32,
+    Br=Bc=16, with and without the causal mask, to 1e-12."""
+    rng = np.random.default_rng(0)
+    Q, K, V = (rng.normal(size=(100, 32)) for _ in range(3))
+    for causal in (False, True):
+        O1, l1 = tiled_forward(Q, K, V, 1 / math.sqrt(32), 16, 16, causal)
+        O2, l2 = attention_fwd(Q[None, None], K[None, None], V[None, None], 1 / math.sqrt(32), causal)
+        assert np.abs(O1 - O2[0, 0]).max() < 1e-12
+        assert np.abs(l1 - l2[0, 0]).max() < 1e-12
+
+
+@pytest.mark.parametrize("Br,Bc", [(7, 5), (32, 64), (100, 3)])
+def test_tiled_equals_naive_other_tiles(Br, Bc):
+    rng = np.random.default_rng(Br * Bc)
+    Q, K, V = (rng.normal(size=(77, 16)) for _ in range(3))
+    for causal in (False, True):
+        O1, l1 = tiled_forward(Q, K, V, 0.25, Br, Bc, causal)
+        O2, l2 = attention_fwd(Q[None, None], K[None, None], V[None, None], 0.25, causal)
+        assert np.abs(O1 - O2[0, 0]).max() < 1e-12
+        assert np.abs(l1 - l2[0, 0]).max() < 1e-12
+
+
+# --- library pins --------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_matches_torch_cpu_sdpa(causal):
+    """Lesson 4, section 5: CPU float64 scaled_dot_product_attention equals the explicit
+    softmax; here it pins the oracle (N=1000, d=64 as in that listing)."""
+    F = torch.nn.functional
+    torch.manual_seed(0)
+    q, k, v = (torch.randn(1, 2, 1000, 64, dtype=torch.float64) for _ in range(3))
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=causal).numpy()
+    O, _ = attention_fwd(q.numpy(), k.numpy(), v.numpy(), 1 / 8.0, causal, row_block=256)
+    assert np.abs(O - ref).max() < 1e-12
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_torch_autograd(causal):
+    """The analytic backward equals torch autograd of CPU float64 SDPA."""
+    F = torch.nn.functional
+    torch.manual_seed(1)
+    B, H, N, d = 2, 3, 200, 32
+    q, k, v = (torch.randn(B, H, N, d, dtype=torch.float64, requires_grad=True) for _ in range(3))
+    do = torch.randn(B, H, N, d, dtype=torch.float64)
+    scale = 0.21
+    out = F.scaled_dot_product_attention(q, k, v, is_causal=causal, scale=scale)
+    out.backward(do)
+    dQ, dK, dV = attention_bwd(q.detach().numpy(), k.detach().numpy(), v.detach().numpy(),
+                               do.numpy(), scale, causal, row_block=64)
+    for mine, ref in ((dQ, q.grad), (dK, k.grad), (dV, v.grad)):
+        assert np.abs(mine - ref.numpy()).max() < 1e-12 * max(1.0, np.abs(ref.numpy()).max())
+
+
+# --- brute force ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,d", [(5, 3), (8, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_finite_differences(N, d, causal):
+    """Gradients of sum(dO * O) by central differences (h = 1e-6) on tiny shapes."""
+    rng = np.random.default_rng(N * 10 + d + causal)
+    Q, K, V, dO = (rng.standard_normal((1, 1, N, d)) for _ in range(4))
+    scale = 0.6
+    dQ, dK, dV = attention_bwd(Q, K, V, dO, scale, causal)
+
+    def loss(Q_, K_, V_):
+        O, _ = attention_fwd(Q_, K_, V_, scale, causal)
+        return float((O * dO).sum())
+
+    h = 1e-6
+    for which, grad in ((0, dQ), (1, dK), (2, dV)):
+        fd = np.zeros_like(grad)
+        for idx in np.ndindex(grad.shape):
+            args_p = [Q.copy(), K.copy(), V.copy()]
+            args_m = [Q.copy(), K.copy(), V.copy()]
+            args_p[which][idx] += h
+            args_m[which][idx] -= h
+            fd[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        err = np.abs(fd - grad).max() / max(np.abs(grad).max(), 1e-3)
+        assert err < 1e-7, (which, err)
+
+
+def test_D_identity():
+    """Lesson 4, backward step 3: D_i = sum_j P_ij dP_ij = dO_i . O_i."""
+    rng = np.random.default_rng(9)
+    B, H, N, d = 1, 2, 150, 16
+    Q, K, V, dO = (rng.standard_normal((B, H, N, d)) for _ in range(4))
+    for causal in (False, True):
+        O, _ = attention_fwd(Q, K, V, 0.25, causal)
+        *_, D = attention_bwd(Q, K, V, dO, 0.25, causal, row_block=40, return_D=True)
+        assert np.abs(D - (dO * O).sum(-1)).max() < 1e-13
+
+
+def test_row_block_does_not_change_result():
+    rng = np.random.default_rng(11)
+    Q, K, V, dO = (rng.standard_normal((1, 1, 97, 8)) for _ in range(4))
+    for causal in (False, True):
+        a = attention_fwd(Q, K, V, 0.3, causal, row_block=97)
+        b = attention_fwd(Q, K, V, 0.3, causal, row_block=10)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+        ga = attention_bwd(Q, K, V, dO, 0.3, causal, row_block=97)
+        gb = attention_bwd(Q, K, V, dO, 0.3, causal, row_block=13)
+        for x, y in zip(ga, gb):
+            assert np.abs(x - y).max() < 1e-13
