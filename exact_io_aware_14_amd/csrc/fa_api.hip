@@ -1,0 +1,105 @@
+// fa_api.hip -- the C ABI of libfa.so: argument checks and kernel dispatch.
+// The contract (layout, ownership, error codes) is documented in include/fa.h.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr size_t kWsAlign = 256;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+fa_status check_sizes(int B, int H, int N, int d, float scale, int causal, int dtype) {
+  if (B < 1 || H < 1 || N < 1) return FA_ERR_INVALID_ARG;
+  // row indices (B*H*N) are kept below 2^31 so every grid fits a 32-bit id
+  if ((long long)B * H * N > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+size_t ws_bytes(int B, int H, int N, int d) {
+  const size_t rows = (size_t)B * H * N;
+  return round_up(rows * sizeof(float), kWsAlign) + round_up(rows * d * sizeof(float), kWsAlign);
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return (1 << 16) | 0; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128, dtype bf16 or fp32)";
+    case FA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+fa_status fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, int B, int H, int N, int d, float softmax_scale,
+                       int causal, int dtype) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  const fa_status st = check_sizes(B, H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int H, int N, int d, float softmax_scale, int causal, int dtype,
+                 void* stream) {
+  const fa_status st = fa_fwd_check(q, k, v, o, lse, B, H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, softmax_scale, causal, dtype, stream};
+  return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (check_sizes(B, H, N, d, 1.0f, 0, dtype) != FA_OK) return 0;
+  return ws_bytes(B, H, N, d);
+}
+
+fa_status fa_bwd_check(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, const void* dq, const void* dk,
+                       const void* dv, const void* workspace, size_t workspace_bytes, int B,
+                       int H, int N, int d, float softmax_scale, int causal, int dtype) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return FA_ERR_INVALID_ARG;
+  const fa_status st = check_sizes(B, H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
+      !aligned4(lse))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_bytes(B, H, N, d)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                 size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
+                 int causal, int dtype, void* stream) {
+  const fa_status st = fa_bwd_check(q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                                    workspace_bytes, B, H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  const size_t rows = (size_t)B * H * N;
+  float* Dvec = (float*)workspace;
+  float* dqacc = (float*)((char*)workspace + round_up(rows * sizeof(float), kWsAlign));
+  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, Dvec, dqacc,
+                B, H, N, d, softmax_scale, causal, dtype, stream};
+  return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // extern "C"

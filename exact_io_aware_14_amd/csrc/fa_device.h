@@ -1,0 +1,121 @@
+// fa_device.h -- device-side building blocks of the attention kernels (gfx950).
+//
+// Matrix products run on the CDNA4 32x32 MFMA instructions with fp32 accumulation:
+//   bf16 operands: v_mfma_f32_32x32x16_bf16 (each lane feeds 8 bf16 of A and of B)
+//   fp32 operands: v_mfma_f32_32x32x2_f32   (each lane feeds 1 float of A and of B)
+//
+// Lane layout of a 32x32 accumulator (16 floats per lane, wave64): lane L holds
+// column  n = L % 32  and, in register r, row  m = 8*(r/4) + 4*(L/32) + (r%4).
+// The contraction index of one instruction is split over the two half-waves
+// g = L/32: the kernels only need A and B to agree on which logical k each
+// (g, slot) carries, so they use two assignments:
+//   natural : slot s of half g carries k = g*EPL + s            (contiguous reads)
+//   c-layout: slot s of instruction j, half g carries the row of accumulator
+//             register j*EPL + s, i.e. k = crow(g, j*EPL + s)   (feeds a product
+//             straight from a previous accumulator, no shuffle needed)
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Row of accumulator register r held by half-wave g.
+__device__ __forceinline__ constexpr int crow(int g, int r) {
+  return 8 * (r >> 2) + 4 * g + (r & 3);
+}
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<__bf16> {
+  static constexpr int KPI = 16;  // contraction length of one instruction
+  static constexpr int EPL = 8;   // operand elements per lane
+  typedef bf16x8_t op_t;
+  static __device__ __forceinline__ f32x16_t mma(op_t a, op_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // EPL contiguous elements starting at p (16-byte aligned).
+  static __device__ __forceinline__ op_t load(const __bf16* p) {
+    return *reinterpret_cast<const op_t*>(p);
+  }
+  // One element per slot from p + offs(s) (strided / gathered operand).
+  template <typename F>
+  static __device__ __forceinline__ op_t gather(const __bf16* p, F offs) {
+    op_t v;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) v[s] = p[offs(s)];
+    return v;
+  }
+  // Operand from accumulator registers r0 .. r0+EPL-1 (rounded to nearest even).
+  static __device__ __forceinline__ op_t from_acc(const f32x16_t& c, int r0) {
+    op_t v;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) v[s] = (__bf16)c[r0 + s];
+    return v;
+  }
+  static __device__ __forceinline__ op_t zero() {
+    op_t v;
+#pragma unroll
+    for (int s = 0; s < EPL; ++s) v[s] = (__bf16)0.0f;
+    return v;
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int KPI = 2;
+  static constexpr int EPL = 1;
+  typedef float op_t;
+  static __device__ __forceinline__ f32x16_t mma(op_t a, op_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ op_t load(const float* p) { return *p; }
+  template <typename F>
+  static __device__ __forceinline__ op_t gather(const float* p, F offs) {
+    return p[offs(0)];
+  }
+  static __device__ __forceinline__ op_t from_acc(const f32x16_t& c, int r0) { return c[r0]; }
+  static __device__ __forceinline__ op_t zero() { return 0.0f; }
+};
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// 16-byte vector copy type.
+struct alignas(16) v16b {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Block id -> logical work id.  Consecutive workgroup ids are spread round robin
+// over the 8 XCDs (each with its own L2); the remap hands each XCD a contiguous
+// range of logical ids, so the tiles of one (batch, head) share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  constexpr int kXcd = 8;
+  if (n % kXcd != 0) return id;
+  return (id % kXcd) * (n / kXcd) + id / kXcd;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+// Start value of the running max: finite, so that exp2((m_old - m_new) * c) and
+// s * c - m * c never form -inf - (-inf) while a row has seen no visible key.
+constexpr float kNoMax = -1.0e30f;
+
+}  // namespace fa

@@ -1,0 +1,120 @@
+/*
+ * fa.h -- C ABI of libfa.so: exact tiled scaled-dot-product attention on AMD
+ * MI355X (gfx950), forward and backward, as hand-written HIP kernels.
+ *
+ * What is computed ("FlashAttention and online softmax", ML Systems Lesson 4):
+ *   forward  -- section "The GPU picture: keep the tile on chip" and the tiled
+ *               forward pass of "The online softmax theorem":
+ *               O = softmax(scale * Q K^T [causal]) V, row by row, and per row
+ *               lse_i = log sum_j exp(scale * q_i . k_j) over the visible keys
+ *               (natural log, the scale included).  The N x N score matrix is
+ *               never written to memory.
+ *   causal   -- section "Causal masks and FlashAttention-3": query i sees key j
+ *               iff j <= i; tiles wholly above the diagonal are skipped.
+ *   backward -- section "Backward pass: recompute instead of store": the score
+ *               tiles are recomputed from Q, K and lse (P = exp(S - lse)), then
+ *               dV = P^T dO, dP = dO V^T, dS = P o (dP - D) with
+ *               D_i = dO_i . O_i, dQ = scale dS K, dK = scale dS^T Q.
+ *               dQ, dK, dV are the gradients of sum(dO o O).
+ *
+ * Layout.  Every [B, H, N, d] tensor is dense and contiguous in that order
+ * (row n of head (b, h) starts at element ((b * H + h) * N + n) * d).  lse is
+ * [B, H, N] float32.  Element type: bf16 (FA_DTYPE_BF16, arithmetic in fp32 with
+ * bf16 operands for the matrix products) or float32 (FA_DTYPE_FP32).
+ *
+ * Ownership.  All pointers are device memory owned by the caller.  The library
+ * never allocates, frees or synchronises: work is enqueued on `stream` (a
+ * hipStream_t; NULL = the legacy default stream) and the call returns at once.
+ * Inputs are read only; outputs are fully overwritten (never accumulated into);
+ * outputs must not alias inputs or each other.  The backward workspace is
+ * scratch owned by the caller, at least fa_bwd_workspace_bytes() bytes; its
+ * contents on entry do not matter and are undefined on exit.  Calls are
+ * reentrant; calls on different streams that share no output run independently.
+ *
+ * Errors.  Arguments are checked on the host before anything is enqueued; a
+ * failed check launches nothing and returns:
+ *   FA_ERR_INVALID_ARG  -- a null pointer, B, H or N < 1, B*H*N >= 2^31, a
+ *                          tensor pointer not 16-byte aligned (lse: 4-byte),
+ *                          softmax_scale not finite and > 0, causal not 0 or 1,
+ *                          or a workspace shorter than fa_bwd_workspace_bytes();
+ *   FA_ERR_UNSUPPORTED  -- d not 64 or 128, or an unknown dtype;
+ *   FA_ERR_LAUNCH       -- the HIP runtime rejected a kernel launch.
+ * There is no fallback path of any kind: an unsupported request fails loudly
+ * ("FlashAttention from Scratch", section "Pitfalls that turn into incidents").
+ *
+ * Numerics.  The forward is bitwise deterministic for given inputs.  The backward
+ * accumulates dQ with float32 atomics, so dQ may differ in the last bits from run
+ * to run; results agree with the exact ones up to rounding, not bitwise (same
+ * page, "Bitwise mismatch is not a bug").
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_LAUNCH = 3
+} fa_status;
+
+typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
+
+/* Forward pass.
+ *   q, k, v : [B, H, N, d] inputs of `dtype`.
+ *   o       : [B, H, N, d] output of `dtype`.
+ *   lse     : [B, H, N] float32 output (natural-log logsumexp of the scaled,
+ *             masked score row).
+ *   softmax_scale : the factor tau in S = tau Q K^T (1/sqrt(d) for standard
+ *             attention); must be finite and > 0.
+ *   causal  : 1 = query i sees keys j <= i; 0 = every key.
+ *   stream  : hipStream_t to enqueue on.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int N, int d, float softmax_scale, int causal,
+                 int dtype, void* stream);
+
+/* Bytes of device workspace fa_bwd needs: one float32 D per row plus a float32
+ * dQ accumulator of [B, H, N, d], each 256-byte aligned.  0 for invalid sizes. */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/* Backward pass.
+ *   q, k, v, o, dout : [B, H, N, d] of `dtype` (o is the forward output and dout
+ *             the gradient of the loss with respect to it).
+ *   lse     : [B, H, N] float32 from fa_fwd on the same q, k, v, scale, causal.
+ *   dq, dk, dv : [B, H, N, d] outputs of `dtype`.
+ *   workspace, workspace_bytes : caller-owned scratch (see above).
+ *   Other arguments as for fa_fwd. */
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                 void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                 float softmax_scale, int causal, int dtype, void* stream);
+
+/* Host-only argument checks of fa_fwd / fa_bwd (same rules, same codes); they
+ * touch no device and enqueue nothing.  Pointers are checked for null and
+ * alignment only. */
+fa_status fa_fwd_check(const void* q, const void* k, const void* v, const void* o,
+                       const float* lse, int B, int H, int N, int d,
+                       float softmax_scale, int causal, int dtype);
+fa_status fa_bwd_check(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, const void* dq,
+                       const void* dk, const void* dv, const void* workspace,
+                       size_t workspace_bytes, int B, int H, int N, int d,
+                       float softmax_scale, int causal, int dtype);
+
+/* Static text for a status code ("unknown status" for other values). */
+const char* fa_status_string(int status);
+
+/* ABI version of this header: (major << 16) | minor. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

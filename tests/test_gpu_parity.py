@@ -1,0 +1,200 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Small cases span several tiles and a ragged tail and are compared element by
+element in full.  The five full-size workloads run at their real shapes with the
+same launch configuration the benchmark times; every output of whole sampled
+heads is compared (a head is the oracle's independent unit of work).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_14_amd import fa
+from exact_io_aware_14_amd.inputs import WORKLOADS, Workload, make_inputs, to_f64
+from oracle import attention_bwd, attention_fwd
+from parity import check_fwd, check_grad, f64
+
+pytestmark = pytest.mark.gpu
+
+TORCH_DT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    fa.lib()  # fail loudly if the native library is missing
+    return torch.device("cuda:0")
+
+
+def gpu_fwd(x, w, dev):
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))  # catches unwritten elements
+    lse = torch.full((w.B, w.H, w.N), float("nan"), dtype=torch.float32, device=dev)
+    fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+    return q, k, v, o, lse
+
+
+def gpu_bwd(q, k, v, o, lse, do, w, dev):
+    nb = fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=dev)  # NaN garbage: must be cleared
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    return fa.bwd(q, k, v, o, do, lse, w.scale, w.causal, workspace=ws, grads=grads)
+
+
+SMALL = [(1, 1, 1), (1, 1, 7), (2, 3, 300), (1, 2, 1000)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "B%dH%dN%d" % s)
+def test_small_fwd_bwd(dev, dtype, d, causal, shape):
+    B, H, N = shape
+    w = Workload("small", B, H, N, d, causal, dtype, True, seed=N + d)
+    say(f"[small] {dtype} B={B} H={H} N={N} d={d} causal={causal}")
+    x = make_inputs(w)
+    q, k, v, o, lse = gpu_fwd(x, w, dev)
+    Q, K, V, dO = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, causal)
+    torch.cuda.synchronize()
+    check_fwd(dtype, o, lse, O_ref, lse_ref, "fwd")
+    do = x["do"].to(dev)
+    dq, dk, dv = gpu_bwd(q, k, v, o, lse, do, w, dev)
+    torch.cuda.synchronize()
+    dQ, dK, dV = attention_bwd(Q, K, V, dO, w.scale, causal)
+    for G, R, n in ((dq, dQ, "dQ"), (dk, dK, "dK"), (dv, dV, "dV")):
+        check_grad(dtype, G, R, n, "bwd")
+
+
+def _full(name):
+    return WORKLOADS[name]
+
+
+HEADS = {
+    "tiny_fp32": [(0, 0)],
+    "gpt2m_fwd": [(0, 0), (7, 15)],
+    "long_causal": [(0, 0), (3, 31)],
+    "train_step": [(0, 0), (3, 15)],
+    "long_context": [(0, 15)],
+}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(dev, name):
+    """Full-size workload on the GPU; every output element of the sampled heads vs the oracle.
+    long_causal also runs the backward (the fwd+bwd headline shape, dO = 4th draw)."""
+    w = _full(name)
+    backward = w.backward
+    say(f"[workload] {name}: B={w.B} H={w.H} N={w.N} d={w.d} causal={w.causal} {w.dtype} bwd={backward}")
+    x = make_inputs(w, with_do=backward)
+    q, k, v, o, lse = gpu_fwd(x, w, dev)
+    if backward:
+        dq, dk, dv = gpu_bwd(q, k, v, o, lse, x["do"].to(dev), w, dev)
+    torch.cuda.synchronize()
+    for (b, h) in HEADS[name]:
+        sl = lambda t: to_f64(t[b:b + 1, h:h + 1])
+        Q, K, V = sl(x["q"]), sl(x["k"]), sl(x["v"])
+        say(f"  oracle head ({b},{h})")
+        O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, w.causal)
+        check_fwd(w.dtype, o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], O_ref, lse_ref, f"{name}({b},{h})")
+        if backward:
+            dQ, dK, dV = attention_bwd(Q, K, V, sl(x["do"]), w.scale, w.causal)
+            for G, R, n in ((dq, dQ, "dQ"), (dk, dK, "dK"), (dv, dV, "dV")):
+                check_grad(w.dtype, G[b:b + 1, h:h + 1], R, n, f"{name}({b},{h})")
+    # outputs of every head are finite and fully written
+    assert torch.isfinite(o).all().item() and torch.isfinite(lse).all().item()
+    if backward:
+        for G in (dq, dk, dv):
+            assert torch.isfinite(G).all().item()
+
+
+def test_planted_row_exercises_rescaling(dev):
+    """The planted query row (scaled x30) has scores far beyond exp's fp32 range
+    unless the running max is subtracted; its output still matches the oracle."""
+    w = _full("long_causal").with_(B=1, H=1)
+    say("[planted] long_causal head (0,0)")
+    x = make_inputs(w, with_do=False)
+    q, k, v, o, lse = gpu_fwd(x, w, dev)
+    torch.cuda.synchronize()
+    row = w.planted[2]
+    Q, K, V = (to_f64(x[n]) for n in ("q", "k", "v"))
+    S = w.scale * Q[0, 0, row] @ K[0, 0, :row + 1].T
+    assert S.max() * math.log2(math.e) > 128  # 2^s would overflow fp32 without the max
+    O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, True)
+    check_fwd("bf16", o[:, :, row:row + 1], lse[:, :, row:row + 1], O_ref[:, :, row:row + 1],
+              lse_ref[:, :, row:row + 1], "planted")
+
+
+def test_fwd_bitwise_deterministic(dev):
+    w = Workload("det", 2, 4, 777, 128, True, "bf16", False, seed=5)
+    say("[determinism] fwd twice")
+    x = make_inputs(w)
+    _, _, _, o1, l1 = gpu_fwd(x, w, dev)
+    _, _, _, o2, l2 = gpu_fwd(x, w, dev)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_invalid_arguments_fail_loudly(dev):
+    say("[errors] invalid arguments through the C ABI")
+    q = torch.randn(1, 1, 64, 96, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(fa.FaError) as e:
+        fa.fwd(q, q, q)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED
+    q = torch.randn(1, 1, 64, 64, device=dev, dtype=torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 1, 64, device=dev)
+    L = fa.lib()
+    st = L.fa_fwd(q.data_ptr() + 2, q.data_ptr(), q.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                  1, 1, 64, 64, 0.125, 0, fa.FA_DTYPE_BF16, torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        fa.fwd(q.half(), q.half(), q.half())
+
+
+def test_autograd_saves_linear_memory(dev):
+    """What the fused method keeps for backward at N=1000, d=64, fp32: Q, K, V, O
+    and the lse, 1,028,000 bytes ("FlashAttention and online softmax", section 5)."""
+    say("[saved bytes] N=1000 d=64 fp32")
+    torch.manual_seed(0)
+    x = [torch.randn(1, 1, 1000, 64, device=dev, requires_grad=True) for _ in range(3)]
+    seen = {}
+
+    def pack(t):
+        seen[t.untyped_storage().data_ptr()] = t.untyped_storage().nbytes()
+        return t
+
+    with torch.autograd.graph.saved_tensors_hooks(pack, lambda t: t):
+        out = fa.attention(*x)
+    assert sum(seen.values()) == 1028000
+    out.sum().backward()
+    assert all(torch.isfinite(t.grad).all().item() for t in x)
+
+
+@pytest.mark.timeout(300)
+def test_memory_stays_linear_long_context(dev):
+    """N=16384, d=128, 16 heads: the device memory high-water mark of fwd+bwd is the
+    O(N) buffers, far below the 8 GiB one materialised bf16 score matrix set needs."""
+    w = _full("long_context")
+    say("[memory] long_context fwd+bwd")
+    x = make_inputs(w)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base = torch.cuda.memory_allocated(dev)
+    o, lse = fa.fwd(q, k, v, w.scale, True)
+    dq, dk, dv = fa.bwd(q, k, v, o, do, lse, w.scale, True)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated(dev) - base
+    tensor = q.numel() * q.element_size()
+    ws = fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype)
+    expect = 4 * tensor + lse.numel() * 4 + ws  # o, dq, dk, dv + lse + workspace
+    assert peak <= expect + (8 << 20), (peak, expect)
+    assert peak < (8 << 30) // 8
