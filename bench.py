@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one forward (fa_fwd) and one backward (fa_bwd: preprocess, main,
+finalize) over the workload's batch, inputs resident in HBM.  Default workload:
+the long causal layer B=4, H=32, N=4096, d=128, bf16 (planted query row), with
+dO as the fourth seeded draw.  FLOPs credited: forward 4*B*H*N^2*d halved for
+causal, backward 2.5x that.
+
+Prints one JSON line.  ``value`` is forward+backward TFLOP/s over the timed
+steps (wall clock between device synchronisations).  ``roofline`` covers the
+kernel with the largest average duration, timed with HIP events on the stream it
+runs on.  ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the
+same workload (whole heads).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, N=4096 d=128) + % MFMA peak"
+PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CSRC = os.path.join(ROOT, "exact_io_aware_14_amd", "csrc")
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(x, w, heads, outs):
+    """Time the oracle (fwd + bwd, fp64, naive) on whole heads of the workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from exact_io_aware_14_amd.accounting import fwd_flops
+    from exact_io_aware_14_amd.inputs import to_f64
+    from oracle import attention_bwd, attention_fwd
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t = 0.0
+    worst = {"O": 0.0, "lse": 0.0, "dQ": 0.0, "dK": 0.0, "dV": 0.0}
+    o, lse, dq, dk, dv = (z.float().cpu().double().numpy() for z in outs)
+    for (b, h) in heads:
+        sl = lambda a: to_f64(a[b:b + 1, h:h + 1])
+        Q, K, V, dO = sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["do"])
+        t0 = time.perf_counter()
+        O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, w.causal)
+        dQ, dK, dV = attention_bwd(Q, K, V, dO, w.scale, w.causal)
+        t += time.perf_counter() - t0
+        worst["O"] = max(worst["O"], float(np.abs(o[b:b + 1, h:h + 1] - O_ref).max()))
+        worst["lse"] = max(worst["lse"], float(np.abs(lse[b:b + 1, h:h + 1] - lse_ref).max()))
+        for n, G, R in (("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
+            rel = float(np.abs(G[b:b + 1, h:h + 1] - R).max() / np.abs(R).max())
+            worst[n] = max(worst[n], rel)
+    credited = 3.5 * fwd_flops(1, 1, w.N, w.d, w.causal) * len(heads)
+    return {
+        "value": credited / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"fwd+bwd of {len(heads)} whole heads (b,h) in {heads[:3]}... of the workload, "
+                  f"N={w.N}, d={w.d}, fp64 numpy; credited FLOPs as for the GPU; {t:.1f} s",
+        "seconds": t,
+    }, {"O_maxabs": worst["O"], "lse_maxabs": worst["lse"], "dQ_rel": worst["dQ"],
+        "dK_rel": worst["dK"], "dV_rel": worst["dV"], "heads": len(heads)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_causal")
+    ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the CPU oracle sample (0 = skip)")
+    args = ap.parse_args(argv)
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the attention hot path here has no multi-GPU "
+              f"path (asked for --gpus {args.gpus}, WORLD_SIZE={world})", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_io_aware_14_amd import fa
+    from exact_io_aware_14_amd.accounting import bwd_flops, fwd_flops
+    from exact_io_aware_14_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    fa.lib()
+    dev = torch.device("cuda:0")
+    w = WORKLOADS[args.workload]
+    x = make_inputs(w, with_do=True)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    stages = fa.bwd_stages(q, k, v, o, do, lse, w.scale, w.causal, ws, grads)
+    names = ["fwd", "bwd_preprocess", "bwd_main", "bwd_finalize"]
+    calls = [lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)] + stages
+
+    def step(evs=None):
+        for i, c in enumerate(calls):
+            if evs is not None:
+                evs[i].record()
+            c()
+        if evs is not None:
+            evs[len(calls)].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+
+    ff = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    bf = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+    bwd_ms = per["bwd_preprocess"] + per["bwd_main"] + per["bwd_finalize"]
+    value = (ff + bf) / (ms_step * 1e-3) / 1e12
+    fwd_t = ff / (per["fwd"] * 1e-3) / 1e12
+    bwd_t = bf / (bwd_ms * 1e-3) / 1e12
+    dom = "fwd" if per["fwd"] >= per["bwd_main"] else "bwd_main"
+    dom_flops = ff if dom == "fwd" else bf
+    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
+    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}
+    traffic = measured_traffic(kernel_names[dom], w.name)
+
+    props = torch.cuda.get_device_properties(dev)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": w.causal, "planted_row": list(w.planted) if w.planted else None,
+                   "step": "fa_fwd + fa_bwd"},
+        "fwd_tflops": round(fwd_t, 2),
+        "fwd_pct_peak": round(100 * fwd_t / PEAK_TFLOPS, 2),
+        "bwd_tflops": round(bwd_t, 2),
+        "bwd_pct_peak": round(100 * bwd_t / PEAK_TFLOPS, 2),
+        "fwd_bwd_pct_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "kernel_ms": {n: round(m, 4) for n, m in per.items()},
+        "roofline": {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(achieved, 2),
+                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+                     "traffic": traffic},
+        "device": props.name,
+    }
+    if args.cpu_heads > 0:
+        heads = [(i // w.H, i % w.H) for i in range(min(args.cpu_heads, w.B * w.H))]
+        cb, par = cpu_baseline(x, w, heads, (o, lse) + grads)
+        rec["cpu_baseline"] = cb
+        rec["parity_sample"] = par
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

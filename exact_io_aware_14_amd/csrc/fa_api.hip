@@ -87,6 +87,17 @@ fa_status fa_bwd_check(const void* q, const void* k, const void* v, const void* 
   return FA_OK;
 }
 
+static fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            void* workspace, int B, int H, int N, int d, float scale, int causal,
+                            int dtype, void* stream) {
+  const size_t rows = (size_t)B * H * N;
+  float* Dvec = (float*)workspace;
+  float* dqacc = (float*)((char*)workspace + round_up(rows * sizeof(float), kWsAlign));
+  return fa::BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, Dvec, dqacc,
+                     B, H, N, d, scale, causal, dtype, stream};
+}
+
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
@@ -94,12 +105,47 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   const fa_status st = fa_bwd_check(q, k, v, o, dout, lse, dq, dk, dv, workspace,
                                     workspace_bytes, B, H, N, d, softmax_scale, causal, dtype);
   if (st != FA_OK) return st;
-  const size_t rows = (size_t)B * H * N;
-  float* Dvec = (float*)workspace;
-  float* dqacc = (float*)((char*)workspace + round_up(rows * sizeof(float), kWsAlign));
-  fa::BwdArgs a{q, k, v, o, dout, lse, dq, dk, dv, Dvec, dqacc,
-                B, H, N, d, softmax_scale, causal, dtype, stream};
-  return fa::launch_bwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d,
+                                 softmax_scale, causal, dtype, stream);
+  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_finalize(a) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
+fa_status fa_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                            size_t workspace_bytes, int B, int H, int N, int d, int dtype,
+                            void* stream) {
+  // the other pointers of the full check are stood in for by `o`
+  const fa_status st = fa_bwd_check(o, o, o, o, dout, (const float*)o, o, o, o, workspace,
+                                    workspace_bytes, B, H, N, d, 1.0f, 0, dtype);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr,
+                                 nullptr, workspace, B, H, N, d, 1.0f, 0, dtype, stream);
+  return fa::launch_bwd_preprocess(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
+                      int causal, int dtype, void* stream) {
+  const fa_status st = fa_bwd_check(q, k, v, q, dout, lse, dk, dk, dv, workspace,
+                                    workspace_bytes, B, H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, lse, nullptr, dk, dv, workspace, B, H,
+                                 N, d, softmax_scale, causal, dtype, stream);
+  return fa::launch_bwd_main(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_finalize(void* dq, void* workspace, size_t workspace_bytes, int B, int H,
+                          int N, int d, float softmax_scale, int dtype, void* stream) {
+  const fa_status st = fa_bwd_check(dq, dq, dq, dq, dq, (const float*)dq, dq, dq, dq, workspace,
+                                    workspace_bytes, B, H, N, d, softmax_scale, 0, dtype);
+  if (st != FA_OK) return st;
+  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq,
+                                 nullptr, nullptr, workspace, B, H, N, d, softmax_scale, 0, dtype,
+                                 stream);
+  return fa::launch_bwd_finalize(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

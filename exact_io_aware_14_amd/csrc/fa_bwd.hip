@@ -244,50 +244,64 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
     }
 }
 
-template <typename T, int D, int NW>
-static hipError_t launch_bwd_cfg(const BwdArgs& a) {
-  using C = BwdCfg<T, D, NW>;
-  hipStream_t st = (hipStream_t)a.stream;
+template <typename T, int D>
+static hipError_t launch_pre_cfg(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
-  {
-    constexpr int TPR = D / (16 / sizeof(T));
-    const long long threads = rows * TPR;
-    const long long blocks = (threads + 255) / 256;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const T*)a.o, (const T*)a.dout, a.Dvec, a.dqacc, rows);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const int nkb = (a.N + C::BKV - 1) / C::BKV;
-    const long long grid = (long long)a.B * a.H * nkb;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_main_kernel<T, D, NW>), dim3((unsigned)grid), dim3(C::NT), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const T*)a.dout, a.lse,
-                       a.Dvec, a.dqacc, (T*)a.dk, (T*)a.dv, a.N, a.scale, a.causal, nkb);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  {
-    const long long n4 = rows * D / 4;
-    const long long blocks = (n4 + 255) / 256;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       a.dqacc, (T*)a.dq, n4, a.scale);
-    return hipGetLastError();
-  }
+  constexpr int TPR = D / (16 / sizeof(T));
+  const long long blocks = (rows * TPR + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)a.stream, (const T*)a.o, (const T*)a.dout, a.Dvec, a.dqacc, rows);
+  return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a) {
+template <typename T, int D, int NW>
+static hipError_t launch_main_cfg(const BwdArgs& a) {
+  using C = BwdCfg<T, D, NW>;
+  const int nkb = (a.N + C::BKV - 1) / C::BKV;
+  const long long grid = (long long)a.B * a.H * nkb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_main_kernel<T, D, NW>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
+                     (const T*)a.dout, a.lse, a.Dvec, a.dqacc, (T*)a.dk, (T*)a.dv, a.N, a.scale,
+                     a.causal, nkb);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_fin_cfg(const BwdArgs& a) {
+  const long long n4 = (long long)a.B * a.H * a.N * a.d / 4;
+  const long long blocks = (n4 + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0,
+                     (hipStream_t)a.stream, a.dqacc, (T*)a.dq, n4, a.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_preprocess(const BwdArgs& a) {
   if (a.dtype == kBF16) {
-    if (a.d == 64) return launch_bwd_cfg<__bf16, 64, 4>(a);
-    if (a.d == 128) return launch_bwd_cfg<__bf16, 128, 4>(a);
+    if (a.d == 64) return launch_pre_cfg<__bf16, 64>(a);
+    if (a.d == 128) return launch_pre_cfg<__bf16, 128>(a);
   } else {
-    if (a.d == 64) return launch_bwd_cfg<float, 64, 4>(a);
-    if (a.d == 128) return launch_bwd_cfg<float, 128, 4>(a);
+    if (a.d == 64) return launch_pre_cfg<float, 64>(a);
+    if (a.d == 128) return launch_pre_cfg<float, 128>(a);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_main(const BwdArgs& a) {
+  if (a.dtype == kBF16) {
+    if (a.d == 64) return launch_main_cfg<__bf16, 64, 4>(a);
+    if (a.d == 128) return launch_main_cfg<__bf16, 128, 4>(a);
+  } else {
+    if (a.d == 64) return launch_main_cfg<float, 64, 4>(a);
+    if (a.d == 128) return launch_main_cfg<float, 128, 4>(a);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_finalize(const BwdArgs& a) {
+  return a.dtype == kBF16 ? launch_fin_cfg<__bf16>(a) : launch_fin_cfg<float>(a);
 }
 
 }  // namespace fa

@@ -31,6 +31,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+// Backward stages (fields of BwdArgs a stage does not use may be null).
+hipError_t launch_bwd_preprocess(const BwdArgs& a);
+hipError_t launch_bwd_main(const BwdArgs& a);
+hipError_t launch_bwd_finalize(const BwdArgs& a);
 
 }  // namespace fa

@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["lib", "fwd", "bwd", "workspace_bytes", "attention", "FaError",
+__all__ = ["lib", "fwd", "bwd", "bwd_stages", "workspace_bytes", "attention", "FaError",
            "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_LAUNCH",
            "FA_DTYPE_BF16", "FA_DTYPE_FP32", "LIB_PATH"]
 
@@ -47,6 +47,12 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
         L.fa_bwd.restype = i
+        L.fa_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
+        L.fa_bwd_preprocess.restype = i
+        L.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+        L.fa_bwd_main.restype = i
+        L.fa_bwd_finalize.argtypes = [vp, vp, sz, i, i, i, i, f, i, vp]
+        L.fa_bwd_finalize.restype = i
         L.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i]
         L.fa_fwd_check.restype = i
         L.fa_bwd_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i]
@@ -126,6 +132,35 @@ def bwd(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
     return dq, dk, dv
+
+
+def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
+    """The three stages of :func:`bwd` as separate calls (same result), returning a
+    list of three callables so a caller can time or interleave them."""
+    _check_same(q, k, v, o, do)
+    B, H, N, d = _dims(q)
+    dq, dk, dv = grads
+    L, dt, st = lib(), _DTYPES[q.dtype], _stream(q.device)
+    wp, wn = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    sc, ca = float(scale), int(bool(causal))
+
+    def pre():
+        r = L.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), wp, wn, B, H, N, d, dt, st)
+        if r != FA_OK:
+            raise FaError(r, "fa_bwd_preprocess")
+
+    def main():
+        r = L.fa_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                          dk.data_ptr(), dv.data_ptr(), wp, wn, B, H, N, d, sc, ca, dt, st)
+        if r != FA_OK:
+            raise FaError(r, "fa_bwd_main")
+
+    def fin():
+        r = L.fa_bwd_finalize(dq.data_ptr(), wp, wn, B, H, N, d, sc, dt, st)
+        if r != FA_OK:
+            raise FaError(r, "fa_bwd_finalize")
+
+    return [pre, main, fin]
 
 
 class _Attention(torch.autograd.Function):

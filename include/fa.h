@@ -95,6 +95,28 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                  float softmax_scale, int causal, int dtype, void* stream);
 
+/* The three stages fa_bwd runs, in this order, on one stream; a caller may run
+ * them separately (e.g. to time or overlap them).  Same arguments, checks and
+ * codes as fa_bwd for the pointers each stage takes.
+ *   fa_bwd_preprocess : D_i = dO_i . O_i (the row term of dS = P o (dP - D),
+ *                       "Backward pass: recompute instead of store", step 3) into
+ *                       the workspace, and clears the workspace's dQ accumulator.
+ *   fa_bwd_main       : per block of keys, recomputes S and P = exp(S - lse) for
+ *                       every visible query tile, accumulates dK and dV on chip and
+ *                       writes them, and adds the unscaled dS K contributions to
+ *                       the dQ accumulator (steps 1-4 of the same passage).
+ *   fa_bwd_finalize   : dQ = softmax_scale * accumulator, rounded to `dtype`. */
+fa_status fa_bwd_preprocess(const void* o, const void* dout, void* workspace,
+                            size_t workspace_bytes, int B, int H, int N, int d,
+                            int dtype, void* stream);
+fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, void* dk, void* dv, void* workspace,
+                      size_t workspace_bytes, int B, int H, int N, int d,
+                      float softmax_scale, int causal, int dtype, void* stream);
+fa_status fa_bwd_finalize(void* dq, void* workspace, size_t workspace_bytes, int B,
+                          int H, int N, int d, float softmax_scale, int dtype,
+                          void* stream);
+
 /* Host-only argument checks of fa_fwd / fa_bwd (same rules, same codes); they
  * touch no device and enqueue nothing.  Pointers are checked for null and
  * alignment only. */

@@ -198,3 +198,21 @@ def test_memory_stays_linear_long_context(dev):
     expect = 4 * tensor + lse.numel() * 4 + ws  # o, dq, dk, dv + lse + workspace
     assert peak <= expect + (8 << 20), (peak, expect)
     assert peak < (8 << 30) // 8
+
+
+def test_bwd_stages_equal_fa_bwd(dev):
+    """fa_bwd_preprocess + fa_bwd_main + fa_bwd_finalize reproduce fa_bwd."""
+    w = Workload("stages", 1, 3, 500, 128, True, "bf16", True, seed=7)
+    say("[stages] bwd in three calls vs one")
+    x = make_inputs(w)
+    q, k, v, o, lse = gpu_fwd(x, w, dev)
+    do = x["do"].to(dev)
+    dq1, dk1, dv1 = fa.bwd(q, k, v, o, do, lse, w.scale, True)
+    ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    for stage in fa.bwd_stages(q, k, v, o, do, lse, w.scale, True, ws, grads):
+        stage()
+    torch.cuda.synchronize()
+    dq2, dk2, dv2 = grads
+    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
+    check_grad("bf16", dq2, f64(dq1), "dQ", "stages")
