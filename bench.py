@@ -3,8 +3,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one forward (fa_fwd) and one backward (fa_bwd: preprocess, main,
-finalize) over the workload's batch, inputs resident in HBM.  Default workload:
+One step = one forward (fa_fwd) and one backward (fa_bwd: preprocess, main = dK
+and dV, dq) over the workload's batch, inputs resident in HBM.  Default workload:
 the long causal layer B=4, H=32, N=4096, d=128, bf16 (planted query row), with
 dO as the fourth seeded draw.  FLOPs credited: forward 4*B*H*N^2*d halved for
 causal, backward 2.5x that.
@@ -12,8 +12,10 @@ causal, backward 2.5x that.
 Prints one JSON line.  ``value`` is forward+backward TFLOP/s over the timed
 steps (wall clock between device synchronisations).  ``roofline`` covers the
 kernel with the largest average duration, timed with HIP events on the stream it
-runs on.  ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the
-same workload (whole heads).
+runs on; its FLOPs are the matrix products that kernel performs (forward: 2 per
+score, dK/dV pass: 4, dQ pass: 3; each 2*d FLOPs per visible score).
+``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
+workload (whole heads).
 """
 from __future__ import annotations
 
@@ -127,7 +129,7 @@ def main(argv=None) -> int:
     grads = tuple(torch.empty_like(q) for _ in range(3))
     ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
     stages = fa.bwd_stages(q, k, v, o, do, lse, w.scale, w.causal, ws, grads)
-    names = ["fwd", "bwd_preprocess", "bwd_main", "bwd_finalize"]
+    names = ["fwd", "bwd_preprocess", "bwd_main", "bwd_dq"]
     calls = [lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)] + stages
 
     def step(evs=None):
@@ -152,14 +154,15 @@ def main(argv=None) -> int:
 
     ff = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
     bf = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
-    bwd_ms = per["bwd_preprocess"] + per["bwd_main"] + per["bwd_finalize"]
+    bwd_ms = per["bwd_preprocess"] + per["bwd_main"] + per["bwd_dq"]
     value = (ff + bf) / (ms_step * 1e-3) / 1e12
     fwd_t = ff / (per["fwd"] * 1e-3) / 1e12
     bwd_t = bf / (bwd_ms * 1e-3) / 1e12
-    dom = "fwd" if per["fwd"] >= per["bwd_main"] else "bwd_main"
-    dom_flops = ff if dom == "fwd" else bf
-    achieved = dom_flops / (per[dom] * 1e-3) / 1e12
-    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel"}
+    # algorithmic FLOPs each kernel performs: 2*d per visible score per product
+    kflops = {"fwd": ff, "bwd_main": 2.0 * ff, "bwd_dq": 1.5 * ff}
+    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel", "bwd_dq": "bwd_dq_kernel"}
+    dom = max(kflops, key=lambda n: per[n])
+    achieved = kflops[dom] / (per[dom] * 1e-3) / 1e12
     traffic = measured_traffic(kernel_names[dom], w.name)
 
     props = torch.cuda.get_device_properties(dev)

@@ -25,9 +25,15 @@ fa_status check_sizes(int B, int H, int N, int d, float scale, int causal, int d
   return FA_OK;
 }
 
-size_t ws_bytes(int B, int H, int N, int d) {
-  const size_t rows = (size_t)B * H * N;
-  return round_up(rows * sizeof(float), kWsAlign) + round_up(rows * d * sizeof(float), kWsAlign);
+// Workspace: D [B*H*Npad] | lse*log2(e) [B*H*Npad] (both dtypes), then for fp32
+// only a dQ accumulator [B*H*Npad*d]; all float32, each region 256-byte aligned.
+size_t vec_bytes(int B, int H, int N) {
+  return round_up((size_t)B * H * fa::pad_rows(N) * sizeof(float), kWsAlign);
+}
+size_t ws_bytes(int B, int H, int N, int d, int dtype) {
+  const size_t prows = (size_t)B * H * fa::pad_rows(N);
+  const size_t acc = dtype == FA_DTYPE_FP32 ? round_up(prows * d * sizeof(float), kWsAlign) : 0;
+  return 2 * vec_bytes(B, H, N) + acc;
 }
 
 }  // namespace
@@ -68,7 +74,7 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype) {
   if (check_sizes(B, H, N, d, 1.0f, 0, dtype) != FA_OK) return 0;
-  return ws_bytes(B, H, N, d);
+  return ws_bytes(B, H, N, d, dtype);
 }
 
 fa_status fa_bwd_check(const void* q, const void* k, const void* v, const void* o,
@@ -83,7 +89,7 @@ fa_status fa_bwd_check(const void* q, const void* k, const void* v, const void* 
       !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned16(workspace) ||
       !aligned4(lse))
     return FA_ERR_INVALID_ARG;
-  if (workspace_bytes < ws_bytes(B, H, N, d)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < ws_bytes(B, H, N, d, dtype)) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 
@@ -91,11 +97,12 @@ static fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const v
                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
                             void* workspace, int B, int H, int N, int d, float scale, int causal,
                             int dtype, void* stream) {
-  const size_t rows = (size_t)B * H * N;
+  const size_t vb = vec_bytes(B, H, N);
   float* Dvec = (float*)workspace;
-  float* dqacc = (float*)((char*)workspace + round_up(rows * sizeof(float), kWsAlign));
-  return fa::BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, Dvec, dqacc,
-                     B, H, N, d, scale, causal, dtype, stream};
+  float* L2 = (float*)((char*)workspace + vb);
+  float* dqacc = dtype == FA_DTYPE_FP32 ? (float*)((char*)workspace + 2 * vb) : nullptr;
+  return fa::BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, Dvec, L2, dqacc,
+                     B, H, N, d, fa::pad_rows(N), scale, causal, dtype, stream};
 }
 
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -109,43 +116,43 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                                  softmax_scale, causal, dtype, stream);
   if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
   if (fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_finalize(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
   return FA_OK;
 }
 
-fa_status fa_bwd_preprocess(const void* o, const void* dout, void* workspace,
-                            size_t workspace_bytes, int B, int H, int N, int d, int dtype,
-                            void* stream) {
-  // the other pointers of the full check are stood in for by `o`
-  const fa_status st = fa_bwd_check(o, o, o, o, dout, (const float*)o, o, o, o, workspace,
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                            void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                            int dtype, void* stream) {
+  // the pointers this stage does not take are stood in for by `o` in the full check
+  const fa_status st = fa_bwd_check(o, o, o, o, dout, lse, o, o, o, workspace,
                                     workspace_bytes, B, H, N, d, 1.0f, 0, dtype);
   if (st != FA_OK) return st;
-  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, dout, nullptr, nullptr, nullptr,
+  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, o, dout, lse, nullptr, nullptr,
                                  nullptr, workspace, B, H, N, d, 1.0f, 0, dtype, stream);
   return fa::launch_bwd_preprocess(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                      const float* lse, void* dk, void* dv, void* workspace,
-                      size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
-                      int causal, int dtype, void* stream) {
-  const fa_status st = fa_bwd_check(q, k, v, q, dout, lse, dk, dk, dv, workspace,
+                      void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+                      int H, int N, int d, float softmax_scale, int causal, int dtype,
+                      void* stream) {
+  const fa_status st = fa_bwd_check(q, k, v, q, dout, (const float*)q, dk, dk, dv, workspace,
                                     workspace_bytes, B, H, N, d, softmax_scale, causal, dtype);
   if (st != FA_OK) return st;
-  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, lse, nullptr, dk, dv, workspace, B, H,
-                                 N, d, softmax_scale, causal, dtype, stream);
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv, workspace, B,
+                                 H, N, d, softmax_scale, causal, dtype, stream);
   return fa::launch_bwd_main(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-fa_status fa_bwd_finalize(void* dq, void* workspace, size_t workspace_bytes, int B, int H,
-                          int N, int d, float softmax_scale, int dtype, void* stream) {
-  const fa_status st = fa_bwd_check(dq, dq, dq, dq, dq, (const float*)dq, dq, dq, dq, workspace,
-                                    workspace_bytes, B, H, N, d, softmax_scale, 0, dtype);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                    void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
+                    float softmax_scale, int causal, int dtype, void* stream) {
+  const fa_status st = fa_bwd_check(q, k, v, q, dout, (const float*)q, dq, dq, dq, workspace,
+                                    workspace_bytes, B, H, N, d, softmax_scale, causal, dtype);
   if (st != FA_OK) return st;
-  const fa::BwdArgs a = bwd_args(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, dq,
-                                 nullptr, nullptr, workspace, B, H, N, d, softmax_scale, 0, dtype,
-                                 stream);
-  return fa::launch_bwd_finalize(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, workspace,
+                                 B, H, N, d, softmax_scale, causal, dtype, stream);
+  return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

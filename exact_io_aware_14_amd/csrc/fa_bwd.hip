@@ -7,14 +7,17 @@
 //   dV_j += P^T dO_i,  dP = dO_i V_j^T,  dS = P o (dP - D_i),
 //   dQ_i += tau dS K_j,  dK_j += tau dS^T Q_i,   with D_i = dO_i . O_i.
 //
-// Three kernels on the caller's stream:
-//   1. bwd_pre:     D = rowsum(dO o O) in fp32 and a zeroed fp32 dQ accumulator.
-//   2. bwd_main:    one workgroup per (batch, head, block of 32*NW keys).  K_j and
+// Three stages on the caller's stream:
+//   1. bwd_pre:     D = rowsum(dO o O) and lse in base 2 per padded row, in fp32
+//                   (both dtypes); for fp32 also a zeroed fp32 dQ accumulator.
+//   2. main:        dK and dV.  bf16: fa_bwd_bf16.hip.  fp32: bwd_main_kernel below,
+//                   one workgroup per (batch, head, block of 32*NW keys); K_j and
 //                   V_j stay in registers, dK_j and dV_j accumulate in registers;
-//                   query tiles stream through LDS.  Each wave owns 32 keys, so
-//                   dK/dV never need a cross-wave reduction.  dQ contributions are
+//                   query tiles stream through LDS; each wave owns 32 keys, so
+//                   dK/dV never need a cross-wave reduction; dQ contributions are
 //                   added with fp32 atomics into the accumulator.
-//   3. dq_convert:  dQ = tau * accumulator, rounded to the storage dtype.
+//   3. dQ:          bf16: the query-stationary dQ pass (fa_bwd_dq_bf16.hip).
+//                   fp32: dq_convert, dQ = tau * accumulator.
 //
 // gfx950 mapping.  S = Q K^T and dP = dO V^T are computed with keys on the lane
 // columns of the 32x32 MFMA accumulator, which makes P^T and dS^T valid A operands
@@ -28,44 +31,60 @@
 namespace fa {
 
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO o O); zero the dQ accumulator.
+// 1. D = rowsum(dO o O), L2 = lse * log2(e) per padded row (D = 0, L2 = +inf on
+//    the padding rows N .. Npad-1 of each head); zero the dQ accumulator.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       const T* __restrict__ dO,
+                                                      const float* __restrict__ LSE,
                                                       float* __restrict__ Dvec,
-                                                      float* __restrict__ dqacc,
-                                                      long long rows) {
+                                                      float* __restrict__ L2,
+                                                      float* __restrict__ dqacc, int N,
+                                                      int Npad, long long prow_total) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int TPR = D / VEC;  // threads per row (divides 64)
   static_assert(64 % TPR == 0, "a row's threads must sit in one wave");
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long row = gid / TPR;
+  const long long prow = gid / TPR;  // padded row index (bh * Npad + q)
   const int part = (int)(gid % TPR);
+  const long long bh = prow / Npad;
+  const int q = (int)(prow - bh * Npad);
+  const bool live = prow < prow_total && q < N;
   float acc = 0.0f;
-  if (row < rows) {
-    const size_t off = (size_t)row * D + part * VEC;
+  if (live) {
+    const size_t off = (size_t)(bh * N + q) * D + part * VEC;
     const T* po = O + off;
     const T* pd = dO + off;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) acc = fmaf(to_f32(po[e]), to_f32(pd[e]), acc);
-    float4* z = reinterpret_cast<float4*>(dqacc + off);
+  }
+  if (dqacc != nullptr && prow < prow_total) {  // Npad accumulator rows per head: clear all
+    float4* z = reinterpret_cast<float4*>(dqacc + (size_t)prow * D + part * VEC);
 #pragma unroll
     for (int e = 0; e < VEC / 4; ++e) z[e] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  if (row < rows && part == 0) Dvec[row] = acc;
+  if (prow < prow_total && part == 0) {
+    Dvec[prow] = live ? acc : 0.0f;
+    L2[prow] = live ? LSE[bh * N + q] * kLog2e : INFINITY;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = scale * accumulator in the storage dtype (4 elements per thread).
+// 3. dQ = scale * accumulator in the storage dtype (4 elements per thread).  The
+//    accumulator has Npad rows per head; only rows < N are converted.
 template <typename T>
 __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
                                                          T* __restrict__ dQ, long long n4,
+                                                         int N, int Npad, int d4,
                                                          float scale) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // over B*H*N*d/4
   if (i >= n4) return;
-  const float4 v = reinterpret_cast<const float4*>(acc)[i];
+  const long long row = i / d4;  // bh * N + q
+  const long long bh = row / N;
+  const long long prow = row + bh * (Npad - N);
+  const float4 v = reinterpret_cast<const float4*>(acc)[prow * d4 + (i - row * d4)];
   T* p = dQ + i * 4;
   p[0] = from_f32<T>(v.x * scale);
   p[1] = from_f32<T>(v.y * scale);
@@ -93,9 +112,9 @@ struct BwdCfg {
 template <typename T, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const T* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dvec,
-    float* __restrict__ dqacc, T* __restrict__ dK, T* __restrict__ dV, int N, float scale,
-    int causal, int nkb) {
+    const T* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
+    float* __restrict__ dqacc, T* __restrict__ dK, T* __restrict__ dV, int N, int Npad,
+    float scale, int causal, int nkb) {
   using C = BwdCfg<T, D, NW>;
   using M = Mma<T>;
   typedef typename M::op_t op_t;
@@ -117,7 +136,6 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
   const int bh = id / nkb;
   const int kb = id - bh * nkb;  // ascending: under a causal mask block 0 has the most work
   const size_t head = (size_t)bh * N * D;
-  const size_t hrow = (size_t)bh * N;
   const int k0 = kb * C::BKV;
   const int kw = k0 + w * 32;  // first key of this wave
   const int mykey = kw + l32;
@@ -171,10 +189,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
       *reinterpret_cast<v16b*>(Qs + r * C::LDQ + col) = xq;
       *reinterpret_cast<v16b*>(dOs + r * C::LDQ + col) = xd;
     }
-    if (tid < C::BQ) {
-      const int q = qb0 + tid;
-      lse_s[tid] = q < N ? LSE[hrow + q] * kLog2e : INFINITY;
-      D_s[tid] = q < N ? Dvec[hrow + q] : 0.0f;
+    if (tid < C::BQ) {  // padded vectors: rows past N hold lse = +inf, D = 0
+      lse_s[tid] = L2[(size_t)bh * Npad + qb0 + tid];
+      D_s[tid] = Dvec[(size_t)bh * Npad + qb0 + tid];
     }
     __syncthreads();
 
@@ -224,9 +241,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
     for (int kk = 0; kk < KPART / KPI; ++kk)
       dq = M::mma(M::load(arow + kk * KPI), M::load(brow + kk * KPI), dq);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
+    for (int r = 0; r < 16; ++r) {  // padded accumulator rows: no bounds test
       const int q = qb0 + crow(g, r);
-      if (q < N) unsafeAtomicAdd(dqacc + (hrow + q) * D + dq_dt * 32 + l32, dq[r]);
+      unsafeAtomicAdd(dqacc + ((size_t)bh * Npad + q) * D + dq_dt * 32 + l32, dq[r]);
     }
   }
 
@@ -246,12 +263,13 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
 
 template <typename T, int D>
 static hipError_t launch_pre_cfg(const BwdArgs& a) {
-  const long long rows = (long long)a.B * a.H * a.N;
+  const long long prows = (long long)a.B * a.H * a.Npad;
   constexpr int TPR = D / (16 / sizeof(T));
-  const long long blocks = (rows * TPR + 255) / 256;
+  const long long blocks = (prows * TPR + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
-                     (hipStream_t)a.stream, (const T*)a.o, (const T*)a.dout, a.Dvec, a.dqacc, rows);
+                     (hipStream_t)a.stream, (const T*)a.o, (const T*)a.dout, a.lse, a.Dvec, a.L2,
+                     a.dqacc, a.N, a.Npad, prows);
   return hipGetLastError();
 }
 
@@ -263,8 +281,8 @@ static hipError_t launch_main_cfg(const BwdArgs& a) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_main_kernel<T, D, NW>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (const T*)a.dout, a.lse, a.Dvec, a.dqacc, (T*)a.dk, (T*)a.dv, a.N, a.scale,
-                     a.causal, nkb);
+                     (const T*)a.dout, a.L2, a.Dvec, a.dqacc, (T*)a.dk, (T*)a.dv, a.N, a.Npad,
+                     a.scale, a.causal, nkb);
   return hipGetLastError();
 }
 
@@ -274,7 +292,8 @@ static hipError_t launch_fin_cfg(const BwdArgs& a) {
   const long long blocks = (n4 + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0,
-                     (hipStream_t)a.stream, a.dqacc, (T*)a.dq, n4, a.scale);
+                     (hipStream_t)a.stream, a.dqacc, (T*)a.dq, n4, a.N, a.Npad, a.d / 4,
+                     a.scale);
   return hipGetLastError();
 }
 
@@ -291,8 +310,7 @@ hipError_t launch_bwd_preprocess(const BwdArgs& a) {
 
 hipError_t launch_bwd_main(const BwdArgs& a) {
   if (a.dtype == kBF16) {
-    if (a.d == 64) return launch_main_cfg<__bf16, 64, 4>(a);
-    if (a.d == 128) return launch_main_cfg<__bf16, 128, 4>(a);
+    return launch_bwd_main_bf16(a);
   } else {
     if (a.d == 64) return launch_main_cfg<float, 64, 4>(a);
     if (a.d == 128) return launch_main_cfg<float, 128, 4>(a);
@@ -300,8 +318,8 @@ hipError_t launch_bwd_main(const BwdArgs& a) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_finalize(const BwdArgs& a) {
-  return a.dtype == kBF16 ? launch_fin_cfg<__bf16>(a) : launch_fin_cfg<float>(a);
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  return a.dtype == kBF16 ? launch_bwd_dq_bf16(a) : launch_fin_cfg<float>(a);
 }
 
 }  // namespace fa

@@ -1,0 +1,259 @@
+// fa_bwd_bf16.hip -- the bf16 dK/dV pass of the backward, tuned for gfx950.
+//
+// Method ("FlashAttention and online softmax", ML Systems Lesson 4, "Backward pass:
+// recompute instead of store"): one workgroup per block of 128 keys (32 per wave),
+// K_j and V_j in registers, dK_j and dV_j accumulated in registers, query tiles of
+// 32 rows streamed; per tile
+//   S = Q_i K_j^T, P = exp2(S*scale*log2e - lse_i*log2e),  dP = dO_i V_j^T,
+//   dS = P o (dP - D_i),  dV_j += P^T dO_i,  dK_j += dS^T Q_i.
+// dQ is computed by its own query-stationary pass (fa_bwd_dq_bf16.hip), which
+// avoids one float atomic per key block per dQ element.
+//
+// Data movement for CDNA4:
+// * Q_i, dO_i and the tile's lse/D values are double buffered in LDS by
+//   global_load_lds_dwordx4 (the next tile lands while this one is computed).
+// * Q and dO live in LDS row-major with the 16-byte chunk index XOR-swizzled by
+//   f(r).  The same f makes both reads conflict-free on 64 banks: the natural
+//   128-bit reads of 16 consecutive rows at one chunk (A operands of S and dP), and
+//   the transposed ds_read_b64_tr_b16 reads of 4 rows x 32 bytes per 16-lane group
+//   (B operands of dV = P^T dO and dK = dS^T Q).
+// * S = Q K^T and dP = dO V^T put keys on the lane columns of the accumulators, so
+//   P^T and dS^T feed dV and dK as A operands straight from registers.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct BwdFast {
+  static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BKV = 32 * NW;  // keys per workgroup
+  static constexpr int BQ = 32;        // query rows per streamed tile (== kRowPad)
+  static constexpr int CPR = D / 8;    // 16-byte chunks per row
+  static constexpr int QTILE = BQ * D;
+  static constexpr int QLOADS = BQ * CPR / 64 / NW;  // direct loads per wave per Q tile
+  static constexpr int NDT = D / 32;
+  static_assert(BQ == kRowPad, "query tiles are the padded row unit");
+  static_assert(BQ * CPR % (64 * NW) == 0, "tiles split over waves");
+};
+
+// Chunk swizzle of the Q and dO tiles (see the file comment).
+template <int D>
+__device__ __forceinline__ int bswz(int r) {
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t tr_pair(const __bf16* lo, const __bf16* hi) {
+  const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)lo);
+  const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)hi);
+  const bf16x4_t x = __builtin_bit_cast(bf16x4_t, a), y = __builtin_bit_cast(bf16x4_t, b);
+  bf16x8_t r;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    r[t] = x[t];
+    r[4 + t] = y[t];
+  }
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int Npad, float scale, int causal,
+    int nkb) {
+  using C = BwdFast<D>;
+  constexpr int NKK = D / 16;
+  constexpr int NDT = C::NDT;
+  constexpr int CPR = C::CPR;
+
+  __shared__ __attribute__((aligned(1024))) __bf16 Q0[C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Q1[C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 G0[C::QTILE];  // dO
+  __shared__ __attribute__((aligned(1024))) __bf16 G1[C::QTILE];
+  __shared__ __attribute__((aligned(16))) float L0[C::BQ];
+  __shared__ __attribute__((aligned(16))) float L1[C::BQ];
+  __shared__ __attribute__((aligned(16))) float E0[C::BQ];  // D values
+  __shared__ __attribute__((aligned(16))) float E1[C::BQ];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = id / nkb;
+  const int kb = id - bh * nkb;
+  const size_t head = (size_t)bh * N * D;
+  const size_t hpad = (size_t)bh * Npad;
+  const int k0 = kb * C::BKV;
+  const int kw = k0 + w * 32;
+  const int mykey = kw + l32;
+
+  // --- direct-load source offsets ------------------------------------------------
+  // Row-major swizzled tiles: chunk slot s = r*CPR + p holds logical chunk p ^ f(r).
+  int q_row[C::QLOADS], q_col[C::QLOADS];
+#pragma unroll
+  for (int i = 0; i < C::QLOADS; ++i) {
+    const int slot = (w * C::QLOADS + i) * 64 + lane;
+    const int r = slot / CPR, p = slot % CPR;
+    q_row[i] = r;
+    q_col[i] = (p ^ bswz<D>(r)) * 8;
+  }
+  auto issue_q = [&](int qt, __bf16* Qd, __bf16* Gd, float* Ld, float* Ed) {
+    const int qb0 = qt * C::BQ;
+#pragma unroll
+    for (int i = 0; i < C::QLOADS; ++i) {
+      const int row = min(qb0 + q_row[i], N - 1);  // padding rows: any valid row (P = 0 there)
+      dma16(Q + head + (size_t)row * D + q_col[i], Qd + (w * C::QLOADS + i) * 512);
+      dma16(dO + head + (size_t)row * D + q_col[i], Gd + (w * C::QLOADS + i) * 512);
+    }
+    if (w == 0 && lane < C::BQ / 4) dma16(L2 + hpad + qb0 + 4 * lane, Ld);
+    if (w == 1 && lane < C::BQ / 4) dma16(Dvec + hpad + qb0 + 4 * lane, Ed);
+  };
+  // --- per-lane LDS read offsets -------------------------------------------------
+  // Natural A-operand read of row l32, logical chunk 2*kk + g.
+  int nat[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) nat[kk] = l32 * D + (((2 * kk + g) ^ bswz<D>(l32)) << 3);
+  // Transposed reads: lane (G, e, q4) loads 8 bytes of row base + 8h + 4(G>>1) + e at
+  // column col0 + 16(G&1) + 4 q4, base a multiple of 16.  For the swizzled tiles the
+  // chunk depends on h (rows 0-7 vs 8-15 of the 16) and on the 32-column tile.
+  const int G = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+  int trq[2][NDT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int row = 8 * h + 4 * (G >> 1) + e4;
+      const int col = dt * 32 + 16 * (G & 1) + 4 * q4;
+      trq[h][dt] = row * D + ((((col >> 3) ^ bswz<D>(row))) << 3) + (col & 7);
+    }
+
+  // --- K and V of this wave's keys as B operands (natural k order) in registers --
+  bf16x8_t kop[NKK], vop[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    if (mykey < N) {
+      kop[kk] = *reinterpret_cast<const bf16x8_t*>(K + head + (size_t)mykey * D + kk * 16 + g * 8);
+      vop[kk] = *reinterpret_cast<const bf16x8_t*>(V + head + (size_t)mykey * D + kk * 16 + g * 8);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        kop[kk][t] = (__bf16)0.0f;
+        vop[kk][t] = (__bf16)0.0f;
+      }
+    }
+  }
+
+  f32x16_t dk[NDT], dv[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    dk[dt] = zero16();
+    dv[dt] = zero16();
+  }
+  const float c = scale * kLog2e;
+  const int nqt = Npad / C::BQ;
+  const int qt0 = causal ? k0 / C::BQ : 0;  // earlier query rows see none of these keys
+
+  auto tile = [&](int qt, const __bf16* Qb, const __bf16* Gb, const float* Lb, const float* Eb,
+                  __bf16* Qn, __bf16* Gn, float* Ln, float* En) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile qt landed
+    __syncthreads();                     // ... everyone's, and tile qt-1's buffers are free
+    if (qt + 1 < nqt) issue_q(qt + 1, Qn, Gn, Ln, En);
+    const int qb0 = qt * C::BQ;
+    if (causal && kw > qb0 + C::BQ - 1) return;  // all of this wave's keys above the tile
+    {
+      // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes.
+      f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8_t aq = *reinterpret_cast<const bf16x8_t*>(Qb + nat[kk]);
+        const bf16x8_t ag = *reinterpret_cast<const bf16x8_t*>(Gb + nat[kk]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vop[kk], dp, 0, 0, 0);
+      }
+      // P = 2^(s*c - lse2) and dS = P (dP - D).  Query rows crow(g, r): four
+      // consecutive rows per 128-bit read of the padded lse / D vectors.
+      const bool mask_keys = mykey >= N;
+      const bool mask_causal = causal && kw + 31 > qb0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float4 l4 = *reinterpret_cast<const float4*>(Lb + 8 * b + 4 * g);
+        const float4 d4 = *reinterpret_cast<const float4*>(Eb + 8 * b + 4 * g);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 4 * b + t;
+          const bool dead = mask_keys | (mask_causal & (mykey > qb0 + crow(g, r)));
+          const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[t]));
+          s[r] = p;
+          dp[r] = p * (dp[r] - dvv[t]);
+        }
+      }
+      // dV += P^T dO and dK += dS^T Q: keys x dims, contraction over the 32 queries.
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8_t pa, da;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          pa[t] = (__bf16)s[8 * j + t];
+          da[t] = (__bf16)dp[8 * j + t];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8_t bg = tr_pair(Gb + j * 16 * D + trq[0][dt], Gb + j * 16 * D + trq[1][dt]);
+          const bf16x8_t bq = tr_pair(Qb + j * 16 * D + trq[0][dt], Qb + j * 16 * D + trq[1][dt]);
+          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bg, dv[dt], 0, 0, 0);
+          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, bq, dk[dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
+  issue_q(qt0, Q0, G0, L0, E0);
+  for (int qt = qt0; qt < nqt; qt += 2) {
+    tile(qt, Q0, G0, L0, E0, Q1, G1, L1, E1);
+    if (qt + 1 < nqt) tile(qt + 1, Q1, G1, L1, E1, Q0, G0, L0, E0);
+  }
+
+  // dK (scaled) and dV: lane = dim column, register = key row.
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kw + crow(g, r);
+      if (key < N) {
+        const size_t off = head + (size_t)key * D + dt * 32 + l32;
+        dK[off] = (__bf16)(dk[dt][r] * scale);
+        dV[off] = (__bf16)dv[dt][r];
+      }
+    }
+}
+
+template <int D>
+static hipError_t launch_bwd_bf16_d(const BwdArgs& a) {
+  using C = BwdFast<D>;
+  const int nkb = (a.N + C::BKV - 1) / C::BKV;
+  const long long grid = (long long)a.B * a.H * nkb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_bf16_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
+                     (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dk,
+                     (__bf16*)a.dv, a.N, a.Npad, a.scale, a.causal, nkb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
+  if (a.d == 64) return launch_bwd_bf16_d<64>(a);
+  if (a.d == 128) return launch_bwd_bf16_d<128>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,235 @@
+// fa_bwd_dq_bf16.hip -- the bf16 dQ pass of the backward, tuned for gfx950.
+//
+// dQ_i = scale * sum_j dS_ij K_j with dS = P o (dP - D), P = exp(S - lse)
+// ("FlashAttention and online softmax", ML Systems Lesson 4, "Backward pass:
+// recompute instead of store", steps 1-4).  The dK/dV pass keeps keys stationary;
+// summing its per-key-block dQ contributions would take one float atomic per key
+// block per dQ element, and gfx950 retires about 3.4e11 such atomics per second,
+// well below what the matrix cores need at this shape.  This pass instead keeps a
+// block of 128 query rows stationary (32 per wave), like the forward, and streams
+// K/V tiles, recomputing S and dP: three matrix products per tile and no atomics.
+//
+// Per 64-key tile, transposed products on 32x32 MFMA (queries on lane columns):
+//   S^T  = K Q^T       A: K rows (natural LDS reads),  B: Q^T in registers
+//   dP^T = V dO^T      A: V rows (natural LDS reads),  B: dO^T in registers
+//   dS^T = P^T o (dP^T - D)  with P^T = 2^(S^T c - lse2): lse2 and D are per lane
+//   dQ^T += K^T dS^T   A: K^T (transposed LDS reads),  B: dS^T from the registers
+// K and V tiles are double buffered in LDS by global_load_lds_dwordx4, row-major
+// with the chunk swizzle f(r) that keeps both natural and transposed reads free of
+// bank conflicts.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct DqFast {
+  static constexpr int NW = 4;
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;  // query rows per workgroup
+  static constexpr int BC = 64;       // keys per K/V tile
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BC * D;
+  static constexpr int LOADS = BC * CPR / 64 / NW;
+  static_assert(BC * CPR % (64 * NW) == 0, "tile must split over the waves");
+};
+
+template <int D>
+__device__ __forceinline__ int dq_swz(int r) {
+  return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
+}
+
+__device__ __forceinline__ void dq_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
+    __bf16* __restrict__ dQ, int N, int Npad, float scale, int causal, int nqb) {
+  using C = DqFast<D>;
+  constexpr int NKK = D / 16;
+  constexpr int NDT = D / 32;
+  constexpr int CPR = C::CPR;
+
+  __shared__ __attribute__((aligned(1024))) __bf16 K0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 K1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V1[C::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = id / nqb;
+  int qb = id - bh * nqb;
+  if (causal) qb = nqb - 1 - qb;  // longest query blocks of a head first
+  const size_t head = (size_t)bh * N * D;
+  const int q0 = qb * C::BR;
+  const int qw = q0 + w * 32;
+  const int myq = qw + l32;
+
+  // direct-load sources: slot s = r*CPR + p holds logical chunk p ^ f(r)
+  int src_row[C::LOADS], src_col[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int slot = (w * C::LOADS + i) * 64 + lane;
+    const int r = slot / CPR, p = slot % CPR;
+    src_row[i] = r;
+    src_col[i] = (p ^ dq_swz<D>(r)) * 8;
+  }
+  auto issue_tile = [&](int kt, __bf16* Kd, __bf16* Vd) {
+    const int kbase = kt * C::BC;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int row = min(kbase + src_row[i], N - 1);  // keys past the end are masked
+      dq_dma16(K + head + (size_t)row * D + src_col[i], Kd + (w * C::LOADS + i) * 512);
+      dq_dma16(V + head + (size_t)row * D + src_col[i], Vd + (w * C::LOADS + i) * 512);
+    }
+  };
+  // natural A-operand reads: row ks*32 + l32, logical chunk 2*kk + g
+  int nat[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) nat[kk] = l32 * D + (((2 * kk + g) ^ dq_swz<D>(l32)) << 3);
+  // transposed reads of K (A of dQ^T = K^T dS^T): row 16j + 8h + 4(G>>1) + e,
+  // column dt*32 + 16(G&1) + 4 q4
+  const int G = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+  int trk[2][NDT];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int row = 8 * h + 4 * (G >> 1) + e4;
+      const int col = dt * 32 + 16 * (G & 1) + 4 * q4;
+      trk[h][dt] = row * D + (((col >> 3) ^ dq_swz<D>(row)) << 3) + (col & 7);
+    }
+
+  // Q^T and dO^T operands of this lane's query row, its lse (base 2) and D.
+  bf16x8_t qop[NKK], gop[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    if (myq < N) {
+      qop[kk] = *reinterpret_cast<const bf16x8_t*>(Q + head + (size_t)myq * D + kk * 16 + g * 8);
+      gop[kk] = *reinterpret_cast<const bf16x8_t*>(dO + head + (size_t)myq * D + kk * 16 + g * 8);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        qop[kk][t] = (__bf16)0.0f;
+        gop[kk][t] = (__bf16)0.0f;
+      }
+    }
+  }
+  const float lse2 = L2[(size_t)bh * Npad + min(myq, Npad - 1)];  // +inf past N: P = 0
+  const float dval = Dvec[(size_t)bh * Npad + min(myq, Npad - 1)];
+
+  f32x16_t acc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero16();
+  const float c = scale * kLog2e;
+  const int q_last = min(q0 + C::BR, N) - 1;
+  const int nkt = causal ? q_last / C::BC + 1 : (N + C::BC - 1) / C::BC;
+
+  auto tile = [&](int kt, const __bf16* Kb, const __bf16* Vb, __bf16* Kn, __bf16* Vn) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
+    __syncthreads();                     // ... everyone's, and the other buffers are free
+    if (kt + 1 < nkt) issue_tile(kt + 1, Kn, Vn);
+    const int k0 = kt * C::BC;
+    if (causal && k0 > qw + 31) return;  // tile wholly above this wave's rows
+
+    f32x16_t s[2], dp[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      s[ks] = zero16();
+      dp[ks] = zero16();
+    }
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(Kb + ks * 32 * D + nat[kk]);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(Vb + ks * 32 * D + nat[kk]);
+        s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[kk], s[ks], 0, 0, 0);
+        dp[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gop[kk], dp[ks], 0, 0, 0);
+      }
+    const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + ks * 32 + crow(g, r);
+        const bool dead = need_mask & ((key >= N) | (causal & (key > myq)));
+        const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -lse2));
+        dp[ks][r] = p * (dp[ks][r] - dval);
+      }
+    // dQ^T += K^T dS^T over the tile's 64 keys (4 steps of 16, c-layout key order).
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8_t b;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) b[t] = (__bf16)dp[ks][8 * j + t];
+        const __bf16* kb = Kb + (ks * 32 + j * 16) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(kb + trk[0][dt]));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(kb + trk[1][dt]));
+          const bf16x4_t x = __builtin_bit_cast(bf16x4_t, lo), y = __builtin_bit_cast(bf16x4_t, hi);
+          bf16x8_t a;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            a[t] = x[t];
+            a[4 + t] = y[t];
+          }
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
+        }
+      }
+  };
+
+  issue_tile(0, K0, V0);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(kt, K0, V0, K1, V1);
+    if (kt + 1 < nkt) tile(kt + 1, K1, V1, K0, V0);
+  }
+
+  // dQ = scale * acc: lane = query row, registers = dims 8 rb + 4 g + 0..3 of tile dt.
+  if (myq < N) {
+    __bf16* row = dQ + head + (size_t)myq * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        bf16x4_t v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (__bf16)(acc[dt][4 * rb + t] * scale);
+        *reinterpret_cast<bf16x4_t*>(row + dt * 32 + 8 * rb + 4 * g) = v;
+      }
+  }
+}
+
+template <int D>
+static hipError_t launch_dq_bf16_d(const BwdArgs& a) {
+  using C = DqFast<D>;
+  const int nqb = (a.N + C::BR - 1) / C::BR;
+  const long long grid = (long long)a.B * a.H * nqb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
+                     (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dq,
+                     a.N, a.Npad, a.scale, a.causal, nqb);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
+  if (a.d == 64) return launch_dq_bf16_d<64>(a);
+  if (a.d == 128) return launch_dq_bf16_d<128>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

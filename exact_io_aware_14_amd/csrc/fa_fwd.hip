@@ -253,8 +253,7 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a) {
 
 hipError_t launch_fwd(const FwdArgs& a) {
   if (a.dtype == kBF16) {
-    if (a.d == 64) return launch_fwd_cfg<__bf16, 64, 64, 4, 1>(a);
-    if (a.d == 128) return launch_fwd_cfg<__bf16, 128, 64, 4, 1>(a);
+    return launch_fwd_bf16(a);
   } else {
     if (a.d == 64) return launch_fwd_cfg<float, 64, 32, 4, 1>(a);
     if (a.d == 128) return launch_fwd_cfg<float, 128, 32, 4, 1>(a);

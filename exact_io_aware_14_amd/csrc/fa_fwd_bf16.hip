@@ -1,0 +1,291 @@
+// fa_fwd_bf16.hip -- the bf16 forward kernel tuned for gfx950.
+//
+// Same method as fa_fwd.hip ("FlashAttention and online softmax", ML Systems
+// Lesson 4, the tiled forward pass under "The online softmax theorem"), with the
+// data movement built around CDNA4:
+//
+// * K/V tiles go global -> LDS with global_load_lds_dwordx4 (no staging VGPRs),
+//   double buffered: tile j+1 is in flight while tile j is computed.
+// * LDS has 64 banks of 4 bytes.  K is stored chunk-major inside 16-row groups
+//   (16-byte chunk c of row r at ((r/16)*CPR + c)*16 + r%16 chunks), so the 16
+//   lanes of a 128-bit read phase, which read 16 consecutive rows at one chunk,
+//   touch 256 contiguous bytes.  V is stored row-major with the 16-byte chunk index
+//   XOR-swizzled by the row, and read transposed with ds_read_b64_tr_b16: within
+//   each 16-lane group, lane i receives element i%4 of the 8 bytes loaded by lanes
+//   4e + i/4, e = 0..3.  Each group then reads 4 rows x 32 bytes, and the swizzle
+//   puts the 4 rows of a 32-lane phase on disjoint banks.
+// * The running max used as the softmax reference is only moved when a tile's max
+//   exceeds it by more than 2^8 in the exp2 domain.  The online-softmax theorem's
+//   exactness needs only that l and o~ share one reference value, which stays
+//   true; exponents are bounded by 2^8 instead of 1, far inside fp32 and bf16
+//   range.  The rescale of o~ (64 multiplies per lane) is thereby skipped on
+//   almost every tile.
+// * Waves whose 32 query rows all lie above a diagonal tile skip its math.
+// * The P tile enters the PV product rounded to bf16, so O is normalised by the sum
+//   of those same rounded weights (v_dot2_f32_bf16 against ones): O stays an exact
+//   convex combination of V rows and D = dO . O in the backward matches the P it
+//   recomputes, even for rows whose softmax is nearly one-hot.  lse keeps the sum
+//   of the unrounded weights.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct FwdFast {
+  static constexpr int NW = 4;             // waves per workgroup
+  static constexpr int NT = 64 * NW;
+  static constexpr int BR = 32 * NW;       // query rows per workgroup
+  static constexpr int BC = 64;            // keys per K/V tile
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int TILE = BC * D;      // elements per K (or V) tile
+  static constexpr int LOADS = BC * CPR / 64 / NW;  // direct loads per wave per tile
+  static_assert(BC * CPR % (64 * NW) == 0, "tile must split over the waves");
+  static constexpr float kRescaleLog2 = 8.0f;  // move the reference max past 2^8 growth
+};
+
+// LDS chunk slot of K's 16-byte chunk (r, c): chunk-major inside 16-row groups.
+template <int D>
+__device__ __forceinline__ int k_slot(int r, int c) {
+  return ((r >> 4) * (D / 8) + c) * 16 + (r & 15);
+}
+// V's swizzle: chunk c of row r is stored at chunk c ^ vswz(r) of that row.
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int N, float scale, int causal, int nqb) {
+  using C = FwdFast<D>;
+  constexpr int NKK = D / 16;  // MFMA steps along d
+  constexpr int NDT = D / 32;  // 32-wide dim tiles of O^T
+  constexpr int CPR = C::CPR;
+
+  // Two K and two V buffers as distinct objects, each named statically in the
+  // (twice unrolled) tile loop, so the compiler can see that reading one buffer
+  // does not depend on the direct loads still landing in the other.
+  __shared__ __attribute__((aligned(1024))) __bf16 K0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 K1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 V1[C::TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = id / nqb;
+  int qb = id - bh * nqb;
+  if (causal) qb = nqb - 1 - qb;
+  const size_t head = (size_t)bh * N * D;
+  const __bf16* Kh = K + head;
+  const __bf16* Vh = V + head;
+  const int q0 = qb * C::BR;
+  const int qw = q0 + w * 32;
+  const int myq = qw + l32;
+
+  // --- per-lane address pieces -------------------------------------------------
+  // Direct-load sources: wave w's load i fills chunk slots (w*LOADS + i)*64 + lane.
+  int k_src_row[C::LOADS], k_src_col[C::LOADS], v_src_row[C::LOADS], v_src_col[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int slot = (w * C::LOADS + i) * 64 + lane;
+    // K: slot -> (r, c) inverse of k_slot
+    const int grp = slot / (CPR * 16), within = slot % (CPR * 16);
+    k_src_row[i] = grp * 16 + (within & 15);
+    k_src_col[i] = (within >> 4) * 8;
+    // V: row-major, physical chunk p holds logical chunk p ^ vswz(r)
+    const int r = slot / CPR, p = slot % CPR;
+    v_src_row[i] = r;
+    v_src_col[i] = (p ^ vswz<D>(r)) * 8;
+  }
+  auto issue_tile = [&](int kt, __bf16* Kd, __bf16* Vd) {
+    const int kbase = kt * C::BC;
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int kr = min(kbase + k_src_row[i], N - 1);  // rows past the end: any valid row, masked later
+      const int vr = min(kbase + v_src_row[i], N - 1);
+      __bf16* kdst = Kd + (w * C::LOADS + i) * 64 * 8;
+      __bf16* vdst = Vd + (w * C::LOADS + i) * 64 * 8;
+      lds_dma16(Kh + (size_t)kr * D + k_src_col[i], kdst);
+      lds_dma16(Vh + (size_t)vr * D + v_src_col[i], vdst);
+    }
+  };
+  // K operand read (A of S^T = K Q^T): row ks*32 + l32, chunk 2*kk + g.
+  const int k_rd = k_slot<D>(l32, g) * 8;  // + ks*32 rows and kk*2 chunks are immediates
+  // V^T operand via transposed reads: lane (G = lane/16, e = lane%16/4, q = lane%4)
+  // loads 8 bytes of row rbase + 4*(G>>1) + e at column dt*32 + 16*(G&1) + 4*q.
+  const int G = lane >> 4, e4 = (lane >> 2) & 3, q4 = lane & 3;
+  const int v_row = 4 * (G >> 1) + e4;
+  int v_rd[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) {
+    const int col = dt * 32 + 16 * (G & 1) + 4 * q4;
+    v_rd[dt] = v_row * D + (((col >> 3) ^ vswz<D>(v_row)) << 3) + (col & 7);
+  }
+
+  // --- Q^T operands in registers ---------------------------------------------------
+  bf16x8_t qop[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    if (myq < N) {
+      qop[kk] = *reinterpret_cast<const bf16x8_t*>(Q + head + (size_t)myq * D + kk * 16 + g * 8);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) qop[kk][s] = (__bf16)0.0f;
+    }
+  }
+
+  f32x16_t oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = zero16();
+  float mref = kNoMax, lsum = 0.0f, lsum_bf = 0.0f;
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  const float c = scale * kLog2e;
+  const float grow = C::kRescaleLog2 / c;  // allowed growth of the raw max before a rescale
+
+  const int q_last = min(q0 + C::BR, N) - 1;
+  const int nkt = causal ? q_last / C::BC + 1 : (N + C::BC - 1) / C::BC;
+
+  auto tile = [&](int kt, const __bf16* Kb, const __bf16* Vb, __bf16* Kn, __bf16* Vn) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile kt landed
+    __syncthreads();                     // ... everyone's, and the other buffers are free
+    if (kt + 1 < nkt) issue_tile(kt + 1, Kn, Vn);
+    const int k0 = kt * C::BC;
+    if (causal && k0 > qw + 31) return;  // tile wholly above this wave's rows
+    // S^T = K Q^T
+    f32x16_t s[2];
+    s[0] = zero16();
+    s[1] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            Kb + k_rd + (ks * 2 * CPR * 16 + kk * 2 * 16) * 8);
+        s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], s[ks], 0, 0, 0);
+      }
+
+    const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw);
+    if (need_mask) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + ks * 32 + crow(g, r);
+          if (key >= N || (causal && key > myq)) s[ks][r] = -INFINITY;
+        }
+    }
+
+    // Online softmax: tile max, lazily moved reference, p = 2^(s*c - mref*c).
+    float mx = s[0][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool move = mx > mref + grow;
+    if (__builtin_amdgcn_ballot_w64(move)) {  // wave-uniform: rare after the first tile
+      const float mnew = move ? mx : mref;
+      const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);
+      lsum *= alpha;
+      lsum_bf *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+      mref = mnew;
+    }
+    const float mc = mref * c;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
+        s[ks][r] = p;
+        lsum += p;
+      }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) pb[sl] = (__bf16)s[ks][j * 8 + sl];
+        lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones2, lsum_bf, false);
+        lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones2, lsum_bf, false);
+        lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones2, lsum_bf, false);
+        lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones2, lsum_bf, false);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const __bf16* base = Vb + v_rd[dt] + (ks * 32 + j * 16) * D;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(base));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(base + 8 * D));
+          bf16x8_t a;
+          const bf16x4_t lob = __builtin_bit_cast(bf16x4_t, lo), hib = __builtin_bit_cast(bf16x4_t, hi);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            a[t] = lob[t];
+            a[4 + t] = hib[t];
+          }
+          oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
+        }
+      }
+  };
+
+  issue_tile(0, K0, V0);
+  for (int kt = 0; kt < nkt; kt += 2) {
+    tile(kt, K0, V0, K1, V1);
+    if (kt + 1 < nkt) tile(kt + 1, K1, V1, K0, V0);
+  }
+
+  // Epilogue: O = o~ / l (l of the rounded weights), lse = mref*scale + ln l.
+  const float l_tot = lsum + __shfl_xor(lsum, 32);
+  const float lb_tot = lsum_bf + __shfl_xor(lsum_bf, 32);
+  const float inv = lb_tot > 0.0f ? 1.0f / lb_tot : 0.0f;
+  if (myq < N) {
+    __bf16* orow = O + head + (size_t)myq * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        bf16x4_t v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (__bf16)(oacc[dt][4 * rb + t] * inv);
+        *reinterpret_cast<bf16x4_t*>(orow + dt * 32 + 8 * rb + 4 * g) = v;
+      }
+    if (g == 0) LSE[(size_t)bh * N + myq] = l_tot > 0.0f ? fmaf(mref, scale, logf(l_tot)) : -INFINITY;
+  }
+}
+
+template <int D>
+static hipError_t launch_fwd_bf16_d(const FwdArgs& a) {
+  using C = FwdFast<D>;
+  const int nqb = (a.N + C::BR - 1) / C::BR;
+  const long long grid = (long long)a.B * a.H * nqb;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0,
+                     (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
+                     (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.N, a.scale, a.causal, nqb);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a) {
+  if (a.d == 64) return launch_fwd_bf16_d<64>(a);
+  if (a.d == 128) return launch_fwd_bf16_d<128>(a);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

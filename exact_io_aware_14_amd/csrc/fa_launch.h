@@ -8,6 +8,11 @@ namespace fa {
 
 enum { kBF16 = 0, kFP32 = 1 };
 
+// Per-head row padding of the backward's D and lse workspace vectors: every
+// backward query tile (32 rows) reads whole padded vectors.
+constexpr int kRowPad = 32;
+inline int pad_rows(int N) { return (N + kRowPad - 1) / kRowPad * kRowPad; }
+
 struct FwdArgs {
   const void *q, *k, *v;
   void* o;
@@ -22,18 +27,23 @@ struct BwdArgs {
   const void *q, *k, *v, *o, *dout;
   const float* lse;
   void *dq, *dk, *dv;
-  float* Dvec;   // [B*H*N] workspace: D_i = dO_i . O_i
-  float* dqacc;  // [B*H*N*d] workspace: float32 dQ accumulator
+  float* Dvec;   // [B*H*Npad] workspace: D_i = dO_i . O_i (0 on padding rows)
+  float* L2;     // [B*H*Npad] workspace: lse_i * log2(e) (+inf on padding rows)
+  float* dqacc;  // [B*H*Npad*d] workspace float32 dQ accumulator (fp32 path only; null for bf16)
   int B, H, N, d;
+  int Npad;      // N rounded up to kRowPad
   float scale;
   int causal, dtype;
   void* stream;
 };
 
-hipError_t launch_fwd(const FwdArgs& a);
+hipError_t launch_fwd(const FwdArgs& a);       // dispatches on dtype
+hipError_t launch_fwd_bf16(const FwdArgs& a);  // the gfx950-tuned bf16 kernel
 // Backward stages (fields of BwdArgs a stage does not use may be null).
 hipError_t launch_bwd_preprocess(const BwdArgs& a);
 hipError_t launch_bwd_main(const BwdArgs& a);
-hipError_t launch_bwd_finalize(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
+hipError_t launch_bwd_main_bf16(const BwdArgs& a);  // gfx950-tuned bf16 dK/dV pass
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a);    // gfx950-tuned bf16 dQ pass
 
 }  // namespace fa

@@ -47,12 +47,12 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd.restype = i
         L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
         L.fa_bwd.restype = i
-        L.fa_bwd_preprocess.argtypes = [vp, vp, vp, sz, i, i, i, i, i, vp]
+        L.fa_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, vp]
         L.fa_bwd_preprocess.restype = i
-        L.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+        L.fa_bwd_main.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
         L.fa_bwd_main.restype = i
-        L.fa_bwd_finalize.argtypes = [vp, vp, sz, i, i, i, i, f, i, vp]
-        L.fa_bwd_finalize.restype = i
+        L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+        L.fa_bwd_dq.restype = i
         L.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i]
         L.fa_fwd_check.restype = i
         L.fa_bwd_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i]
@@ -145,22 +145,23 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
     sc, ca = float(scale), int(bool(causal))
 
     def pre():
-        r = L.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), wp, wn, B, H, N, d, dt, st)
+        r = L.fa_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), wp, wn, B, H, N, d, dt, st)
         if r != FA_OK:
             raise FaError(r, "fa_bwd_preprocess")
 
     def main():
-        r = L.fa_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(),
+        r = L.fa_bwd_main(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
                           dk.data_ptr(), dv.data_ptr(), wp, wn, B, H, N, d, sc, ca, dt, st)
         if r != FA_OK:
             raise FaError(r, "fa_bwd_main")
 
-    def fin():
-        r = L.fa_bwd_finalize(dq.data_ptr(), wp, wn, B, H, N, d, sc, dt, st)
+    def dqs():
+        r = L.fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                        wp, wn, B, H, N, d, sc, ca, dt, st)
         if r != FA_OK:
-            raise FaError(r, "fa_bwd_finalize")
+            raise FaError(r, "fa_bwd_dq")
 
-    return [pre, main, fin]
+    return [pre, main, dqs]
 
 
 class _Attention(torch.autograd.Function):

@@ -42,10 +42,11 @@
  * There is no fallback path of any kind: an unsupported request fails loudly
  * ("FlashAttention from Scratch", section "Pitfalls that turn into incidents").
  *
- * Numerics.  The forward is bitwise deterministic for given inputs.  The backward
- * accumulates dQ with float32 atomics, so dQ may differ in the last bits from run
- * to run; results agree with the exact ones up to rounding, not bitwise (same
- * page, "Bitwise mismatch is not a bug").
+ * Numerics.  bf16: forward and backward are bitwise deterministic for given
+ * inputs.  fp32: the backward accumulates dQ with float32 atomics, so dQ may
+ * differ in the last bits from run to run.  Results agree with the exact ones up
+ * to rounding, not bitwise ("FlashAttention from Scratch", "Bitwise mismatch is
+ * not a bug").
  */
 #ifndef FA_H_
 #define FA_H_
@@ -79,8 +80,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int B, int H, int N, int d, float softmax_scale, int causal,
                  int dtype, void* stream);
 
-/* Bytes of device workspace fa_bwd needs: one float32 D per row plus a float32
- * dQ accumulator of [B, H, N, d], each 256-byte aligned.  0 for invalid sizes. */
+/* Bytes of device workspace fa_bwd needs: two float32 vectors of B*H*Npad values
+ * (Npad = N rounded up to a multiple of 32: D_i and lse_i * log2(e)), and for
+ * FA_DTYPE_FP32 also a float32 dQ accumulator of [B, H, Npad, d]; each region
+ * 256-byte aligned.  0 for invalid sizes. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
 /* Backward pass.
@@ -96,26 +99,33 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  float softmax_scale, int causal, int dtype, void* stream);
 
 /* The three stages fa_bwd runs, in this order, on one stream; a caller may run
- * them separately (e.g. to time or overlap them).  Same arguments, checks and
- * codes as fa_bwd for the pointers each stage takes.
+ * them separately (e.g. to time or overlap them).  Same argument rules and codes as
+ * fa_bwd for the pointers each stage takes.
  *   fa_bwd_preprocess : D_i = dO_i . O_i (the row term of dS = P o (dP - D),
- *                       "Backward pass: recompute instead of store", step 3) into
- *                       the workspace, and clears the workspace's dQ accumulator.
- *   fa_bwd_main       : per block of keys, recomputes S and P = exp(S - lse) for
- *                       every visible query tile, accumulates dK and dV on chip and
- *                       writes them, and adds the unscaled dS K contributions to
- *                       the dQ accumulator (steps 1-4 of the same passage).
- *   fa_bwd_finalize   : dQ = softmax_scale * accumulator, rounded to `dtype`. */
-fa_status fa_bwd_preprocess(const void* o, const void* dout, void* workspace,
-                            size_t workspace_bytes, int B, int H, int N, int d,
-                            int dtype, void* stream);
+ *                       "Backward pass: recompute instead of store", step 3) and
+ *                       lse_i in base 2 into the workspace (for FA_DTYPE_FP32 it also
+ *                       clears the workspace's dQ accumulator).
+ *   fa_bwd_main       : dK and dV.  Per block of keys, recomputes S and
+ *                       P = exp(S - lse) for every visible query tile and
+ *                       accumulates dV += P^T dO and dK += scale dS^T Q on chip
+ *                       (steps 1-4 of the same passage).  For FA_DTYPE_FP32 it also
+ *                       adds the unscaled dS K contributions to the accumulator.
+ *   fa_bwd_dq         : dQ.  FA_DTYPE_BF16: per block of query rows, recomputes S,
+ *                       P, dP and dS for every visible key tile and accumulates
+ *                       dQ = scale dS K on chip (no atomics).  FA_DTYPE_FP32:
+ *                       dQ = scale * accumulator.
+ * fa_bwd_main and fa_bwd_dq read the workspace written by fa_bwd_preprocess. */
+fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                            void* workspace, size_t workspace_bytes, int B, int H,
+                            int N, int d, int dtype, void* stream);
 fa_status fa_bwd_main(const void* q, const void* k, const void* v, const void* dout,
-                      const float* lse, void* dk, void* dv, void* workspace,
-                      size_t workspace_bytes, int B, int H, int N, int d,
-                      float softmax_scale, int causal, int dtype, void* stream);
-fa_status fa_bwd_finalize(void* dq, void* workspace, size_t workspace_bytes, int B,
-                          int H, int N, int d, float softmax_scale, int dtype,
-                          void* stream);
+                      void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      int B, int H, int N, int d, float softmax_scale, int causal,
+                      int dtype, void* stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                    void* dq, void* workspace, size_t workspace_bytes, int B, int H,
+                    int N, int d, float softmax_scale, int causal, int dtype,
+                    void* stream);
 
 /* Host-only argument checks of fa_fwd / fa_bwd (same rules, same codes); they
  * touch no device and enqueue nothing.  Pointers are checked for null and

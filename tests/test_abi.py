@@ -24,7 +24,8 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
-                          "fa_fwd_check", "fa_bwd_check", "fa_abi_version"}
+                          "fa_fwd_check", "fa_bwd_check", "fa_abi_version", "fa_bwd_preprocess",
+                          "fa_bwd_main", "fa_bwd_dq"}
     L = ctypes.CDLL(fa.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -73,9 +74,10 @@ def test_fwd_check_codes():
 def test_bwd_check_codes_and_workspace():
     L = fa.lib()
     ws = L.fa_bwd_workspace_bytes(1, 2, 100, 64, 0)
-    rows = 2 * 100
+    padded = 2 * 128  # N = 100 padded to a multiple of 32 per head
     rnd = lambda x: (x + 255) // 256 * 256
-    assert ws == rnd(rows * 4) + rnd(rows * 64 * 4)
+    assert ws == 2 * rnd(padded * 4)  # bf16: D and lse vectors only
+    assert L.fa_bwd_workspace_bytes(1, 2, 100, 64, 1) == 2 * rnd(padded * 4) + rnd(padded * 64 * 4)
     assert L.fa_bwd_workspace_bytes(1, 2, 100, 96, 0) == 0
     assert bwd_check(wsb=ws) == fa.FA_OK
     assert bwd_check(wsb=ws - 1) == fa.FA_ERR_INVALID_ARG
