@@ -19,6 +19,12 @@
 //   (B operands of dV = P^T dO and dK = dS^T Q).
 // * S = Q K^T and dP = dO V^T put keys on the lane columns of the accumulators, so
 //   P^T and dS^T feed dV and dK as A operands straight from registers.
+// * One wave per SIMD (dK and dV alone hold 128 fp32 per lane at d = 128), so the
+//   overlap comes from inside the wave: the loop is software pipelined.  Iteration
+//   i issues S and dP of tile i, then the dV/dK products of tile i-1 (whose P and
+//   dS wait in registers as bf16), which keep the matrix cores busy while tile i's
+//   P and dS are computed on the vector ALUs.  Q/dO/lse/D tiles are therefore
+//   triple buffered: tile i-1 is still read while tile i+1 lands.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -78,12 +84,16 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
 
   __shared__ __attribute__((aligned(1024))) __bf16 Q0[C::QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 Q1[C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Q2[C::QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 G0[C::QTILE];  // dO
   __shared__ __attribute__((aligned(1024))) __bf16 G1[C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 G2[C::QTILE];
   __shared__ __attribute__((aligned(16))) float L0[C::BQ];
   __shared__ __attribute__((aligned(16))) float L1[C::BQ];
+  __shared__ __attribute__((aligned(16))) float L2s[C::BQ];
   __shared__ __attribute__((aligned(16))) float E0[C::BQ];  // D values
   __shared__ __attribute__((aligned(16))) float E1[C::BQ];
+  __shared__ __attribute__((aligned(16))) float E2[C::BQ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -152,6 +162,10 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     }
   }
 
+  // K and V only ever feed the matrix cores, which read A/B operands from AGPRs as
+  // well; keeping them there leaves the VGPRs for operand prefetch.
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+a"(kop[kk]), "+a"(vop[kk]));
   f32x16_t dk[NDT], dv[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
@@ -162,65 +176,135 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   const int nqt = Npad / C::BQ;
   const int qt0 = causal ? k0 / C::BQ : 0;  // earlier query rows see none of these keys
 
+  // P^T and dS^T of the previous tile, as bf16 A operands (j = 0, 1 query halves).
+  // They start at zero, so the first step's dV/dK products add nothing.
+  bf16x8_t pa[2], da[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      pa[j][t] = (__bf16)0.0f;
+      da[j][t] = (__bf16)0.0f;
+    }
+
+  // One pipelined step, a single basic block: tile qt's S, dP, P, dS and tile qt-1's
+  // dV, dK.  Tiles where every key of this wave lies above the diagonal come out
+  // fully masked (P = dS = 0), so no branch is needed for them.
   auto tile = [&](int qt, const __bf16* Qb, const __bf16* Gb, const float* Lb, const float* Eb,
-                  __bf16* Qn, __bf16* Gn, float* Ln, float* En) {
+                  const __bf16* Qp, const __bf16* Gp, __bf16* Qn, __bf16* Gn, float* Ln, float* En) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile qt landed
-    __syncthreads();                     // ... everyone's, and tile qt-1's buffers are free
+    __syncthreads();                     // ... everyone's; tile qt-2's buffers are free
     if (qt + 1 < nqt) issue_q(qt + 1, Qn, Gn, Ln, En);
     const int qb0 = qt * C::BQ;
-    if (causal && kw > qb0 + C::BQ - 1) return;  // all of this wave's keys above the tile
-    {
-      // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes.
-      f32x16_t s = zero16(), dp = zero16();
+
+    // Operand reads for the whole step, issued before any product that uses them:
+    // Q and dO rows (A operands of S and dP) and, from the previous tile's buffers,
+    // dO and Q transposed (B operands of dV and dK).  One LDS latency per step.
+    bf16x8_t aq[NKK], ag[NKK];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8_t aq = *reinterpret_cast<const bf16x8_t*>(Qb + nat[kk]);
-        const bf16x8_t ag = *reinterpret_cast<const bf16x8_t*>(Gb + nat[kk]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, kop[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag, vop[kk], dp, 0, 0, 0);
+    for (int kk = 0; kk < NKK; ++kk) {
+      aq[kk] = *reinterpret_cast<const bf16x8_t*>(Qb + nat[kk]);
+      ag[kk] = *reinterpret_cast<const bf16x8_t*>(Gb + nat[kk]);
+    }
+    bf16x8_t bg[2][NDT], bq[2][NDT];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        bg[j][dt] = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
+        bq[j][dt] = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
       }
-      // P = 2^(s*c - lse2) and dS = P (dP - D).  Query rows crow(g, r): four
-      // consecutive rows per 128-bit read of the padded lse / D vectors.
-      const bool mask_keys = mykey >= N;
-      const bool mask_causal = causal && kw + 31 > qb0;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK + 8 * NDT, 0);
+
+    // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes.
+    f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float4 l4 = *reinterpret_cast<const float4*>(Lb + 8 * b + 4 * g);
-        const float4 d4 = *reinterpret_cast<const float4*>(Eb + 8 * b + 4 * g);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+    for (int kk = 0; kk < NKK; ++kk) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], kop[kk], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[kk], vop[kk], dp, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK, 0);
+
+    // Keys past the end and, on tiles crossing the diagonal, keys above it: S = -inf,
+    // so P = 2^-inf = 0 and dS = 0.  Only those tiles pay for the per-element test.
+    if ((kw + 32 > N) || (causal && kw + 31 > qb0)) {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 4 * b + t;
-          const bool dead = mask_keys | (mask_causal & (mykey > qb0 + crow(g, r)));
-          const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[t]));
-          s[r] = p;
-          dp[r] = p * (dp[r] - dvv[t]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const bool dead = (mykey >= N) | (causal & (mykey > qb0 + crow(g, r)));
+        s[r] = dead ? -INFINITY : s[r];
       }
-      // dV += P^T dO and dK += dS^T Q: keys x dims, contraction over the 32 queries.
+    }
+
+    // The previous tile's dV/dK products, overlapping this tile's softmax below.
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        bf16x8_t pa, da;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          pa[t] = (__bf16)s[8 * j + t];
-          da[t] = (__bf16)dp[8 * j + t];
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8_t bg = tr_pair(Gb + j * 16 * D + trq[0][dt], Gb + j * 16 * D + trq[1][dt]);
-          const bf16x8_t bq = tr_pair(Qb + j * 16 * D + trq[0][dt], Qb + j * 16 * D + trq[1][dt]);
-          dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, bg, dv[dt], 0, 0, 0);
-          dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, bq, dk[dt], 0, 0, 0);
-        }
+      for (int dt = 0; dt < NDT; ++dt) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[j], bg[j][dt], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[j], bq[j][dt], dk[dt], 0, 0, 0);
       }
+
+    // This tile's P = 2^(s*c - lse2) and dS = P (dP - D), on the vector ALUs while
+    // the products above run.  Query rows crow(g, r): four consecutive rows per
+    // 128-bit read of the padded lse / D vectors.
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float4 l4 = *reinterpret_cast<const float4*>(Lb + 8 * b + 4 * g);
+      const float4 d4 = *reinterpret_cast<const float4*>(Eb + 8 * b + 4 * g);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 4 * b + t;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[t]));
+        s[r] = p;
+        dp[r] = p * (dp[r] - dvv[t]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        pa[j][t] = (__bf16)s[8 * j + t];
+        da[j][t] = (__bf16)dp[8 * j + t];
+      }
+    // Order for this part: each dV/dK product followed by a slice of the softmax.
+#pragma unroll
+    for (int i = 0; i < 4 * NDT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
     }
   };
 
+  // The first step reads its "previous" dV/dK operands from Q2/G2, which nothing has
+  // written yet: zero them, since 0 * (an Inf or NaN bit pattern) would not be 0.
+  // The first step's barrier orders these writes before any later load into them.
+  for (int i = tid; i < C::QTILE / 8; i += C::NT) {
+    reinterpret_cast<v16b*>(Q2)[i] = v16b{0, 0, 0, 0};
+    reinterpret_cast<v16b*>(G2)[i] = v16b{0, 0, 0, 0};
+  }
   issue_q(qt0, Q0, G0, L0, E0);
-  for (int qt = qt0; qt < nqt; qt += 2) {
-    tile(qt, Q0, G0, L0, E0, Q1, G1, L1, E1);
-    if (qt + 1 < nqt) tile(qt + 1, Q1, G1, L1, E1, Q0, G0, L0, E0);
+  int qt = qt0;
+  for (; qt + 2 < nqt; qt += 3) {  // whole rotations: no conditional steps in the body
+    tile(qt, Q0, G0, L0, E0, Q2, G2, Q1, G1, L1, E1);
+    tile(qt + 1, Q1, G1, L1, E1, Q0, G0, Q2, G2, L2s, E2);
+    tile(qt + 2, Q2, G2, L2s, E2, Q1, G1, Q0, G0, L0, E0);
+  }
+  if (qt < nqt) tile(qt, Q0, G0, L0, E0, Q2, G2, Q1, G1, L1, E1);
+  if (qt + 1 < nqt) tile(qt + 1, Q1, G1, L1, E1, Q0, G0, Q2, G2, L2s, E2);
+  // dV/dK of the last tile (its buffers are still intact: no further loads were issued)
+  {
+    const int last = (nqt - 1 - qt0) % 3;
+    const __bf16* Qp = last == 0 ? Q0 : last == 1 ? Q1 : Q2;
+    const __bf16* Gp = last == 0 ? G0 : last == 1 ? G1 : G2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const bf16x8_t bg = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
+        const bf16x8_t bq = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[j], bg, dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[j], bq, dk[dt], 0, 0, 0);
+      }
   }
 
   // dK (scaled) and dV: lane = dim column, register = key row.
