@@ -20,7 +20,6 @@ workload (whole heads).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -33,15 +32,6 @@ if ROOT not in sys.path:
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, N=4096 d=128) + % MFMA peak"
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-CSRC = os.path.join(ROOT, "exact_io_aware_14_amd", "csrc")
-
-
-def source_hash() -> str:
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -52,6 +42,8 @@ def measured_traffic(kernel: str, workload: str):
             t = json.load(f)
     except (OSError, ValueError):
         return None
+    from exact_io_aware_14_amd.traffic import source_hash
+
     e = t.get(workload, {}).get(kernel)
     if not e or e.get("source_hash") != source_hash():
         return None
@@ -103,6 +95,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="for rocprofv3 counter passes: a calibration copy, then each kernel once")
     args = ap.parse_args(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -139,6 +133,20 @@ def main(argv=None) -> int:
             c()
         if evs is not None:
             evs[len(calls)].record()
+
+    if args.traffic_run:
+        from exact_io_aware_14_amd.traffic import COPY_BYTES
+
+        src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        step()  # warm-up
+        torch.cuda.synchronize()
+        torch.neg(src, out=dst)  # calibration: reads and writes COPY_BYTES each
+        torch.cuda.synchronize()
+        step()
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_run": w.name, "copy_bytes": COPY_BYTES}), flush=True)
+        return 0
 
     for _ in range(args.warmup):
         step()
