@@ -140,39 +140,37 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const int k0 = kt * C::BC;
     if (causal && k0 > qw + 31) return;  // tile wholly above this wave's rows
 
-    f32x16_t s[2], dp[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      s[ks] = zero16();
-      dp[ks] = zero16();
-    }
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(Kb + ks * 32 * D + nat[kk]);
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(Vb + ks * 32 * D + nat[kk]);
-        s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[kk], s[ks], 0, 0, 0);
-        dp[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gop[kk], dp[ks], 0, 0, 0);
-      }
+    // The tile's two 32-key halves one after the other: half 1's products can run
+    // while half 0's P and dS are computed, and only one half's S and dP are live.
     const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
+      f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(Kb + ks * 32 * D + nat[kk]);
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(Vb + ks * 32 * D + nat[kk]);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gop[kk], dp, 0, 0, 0);
+      }
+      if (need_mask) {  // keys past the end or above the diagonal: S = -inf, P = 0
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + ks * 32 + crow(g, r);
+          s[r] = ((key >= N) | (causal & (key > myq))) ? -INFINITY : s[r];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + ks * 32 + crow(g, r);
-        const bool dead = need_mask & ((key >= N) | (causal & (key > myq)));
-        const float p = dead ? 0.0f : __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -lse2));
-        dp[ks][r] = p * (dp[ks][r] - dval);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+        dp[r] = p * (dp[r] - dval);
       }
-    // dQ^T += K^T dS^T over the tile's 64 keys (4 steps of 16, c-layout key order).
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+      // dQ^T += K^T dS^T over this half's 32 keys (2 steps of 16, c-layout key order).
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8_t b;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) b[t] = (__bf16)dp[ks][8 * j + t];
+        for (int t = 0; t < 8; ++t) b[t] = (__bf16)dp[8 * j + t];
         const __bf16* kb = Kb + (ks * 32 + j * 16) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
@@ -190,6 +188,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
           acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
         }
       }
+    }
   };
 
   issue_tile(0, K0, V0);
