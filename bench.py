@@ -94,7 +94,7 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal")
-    ap.add_argument("--cpu-heads", type=int, default=8, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--cpu-heads", type=int, default=64, help="heads in the CPU oracle sample (0 = skip)")
     ap.add_argument("--traffic-run", action="store_true",
                     help="for rocprofv3 counter passes: a calibration copy, then each kernel once")
     args = ap.parse_args(argv)
