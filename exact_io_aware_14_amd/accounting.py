@@ -65,3 +65,18 @@ def causal_tiles(N: int, Bt: int) -> tuple[int, int]:
     """(computed, total) square tiles of a causal N x N score matrix cut in Bt x Bt tiles."""
     T = -(-N // Bt)
     return T * (T + 1) // 2, T * T
+
+
+def splitkv_blocks(B: int, H: int, num_splits: int) -> int:
+    """Workgroups of a split-KV decoding pass: one per (batch, head, chunk)
+    ("Split-KV for decoding (flash-decoding)")."""
+    return B * H * num_splits
+
+
+def splitkv_bytes(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, num_splits: int) -> dict:
+    """Algorithmic HBM bytes of split-KV decoding: the partial pass reads Q, K, V and
+    writes fp32 (o, lse) partials; the merge reads the partials and writes O, lse."""
+    e = elem_bytes(dtype)
+    part = num_splits * B * H * Nq * (d + 1) * 4
+    return {"partial": B * H * (Nq + 2 * Nk) * d * e + part,
+            "merge": part + B * H * Nq * (d * e + 4)}

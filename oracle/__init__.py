@@ -10,8 +10,11 @@ Parity status: every function is pinned (no "parity unpinned" entry).
 """
 from .attention import attention_fwd, attention_bwd, visible_mask
 from .online import online_softmax, three_pass_softmax_average, merge, tiled_forward
+from .splitkv import (attention_fwd_rect, merge_partials, split_ranges, splitkv_partials,
+                      visible_rect)
 
 __all__ = [
     "attention_fwd", "attention_bwd", "visible_mask",
     "online_softmax", "three_pass_softmax_average", "merge", "tiled_forward",
+    "attention_fwd_rect", "merge_partials", "split_ranges", "splitkv_partials", "visible_rect",
 ]
