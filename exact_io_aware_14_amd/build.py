@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_bf16.hip", "fa_bwd.hip", "fa_bwd_bf16.hip", "fa_bwd_dq_bf16.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_fwd_bf16.hip", "fa_bwd.hip", "fa_bwd_bf16.hip", "fa_bwd_dq_bf16.hip", "fa_decode.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",

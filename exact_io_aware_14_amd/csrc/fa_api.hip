@@ -36,6 +36,23 @@ size_t ws_bytes(int B, int H, int N, int d, int dtype) {
   return 2 * vec_bytes(B, H, N) + acc;
 }
 
+// Split-KV decoding sizes (see fa.h).
+constexpr int kMaxSplitRows = 8;
+constexpr int kMaxSplits = 256;
+fa_status check_split(int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                      int nsplit, int dtype) {
+  if (Nq < 1 || Nk < 1 || nsplit < 1) return FA_ERR_INVALID_ARG;
+  fa_status st = check_sizes(B, H, Nk, d, scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (Nk < Nq) return FA_ERR_INVALID_ARG;
+  if (Nq > kMaxSplitRows || nsplit > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if ((long long)nsplit * B * H * Nq * (d + 1) > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+size_t split_part_bytes(int B, int H, int Nq, int d, int nsplit) {
+  return round_up((size_t)nsplit * B * H * Nq * d * sizeof(float), kWsAlign);
+}
+
 }  // namespace
 
 extern "C" {
@@ -153,6 +170,60 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
   const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, workspace,
                                  B, H, N, d, softmax_scale, causal, dtype, stream);
   return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
+  if (check_split(B, H, Nq, Nq, d, 1.0f, 0, num_splits, FA_DTYPE_FP32) != FA_OK) return 0;
+  return split_part_bytes(B, H, Nq, d, num_splits) +
+         round_up((size_t)num_splits * B * H * Nq * sizeof(float), kWsAlign);
+}
+
+fa_status fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
+                         float* lse_part, int B, int H, int Nq, int Nk, int d,
+                         float softmax_scale, int causal, int num_splits, int dtype,
+                         void* stream) {
+  if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_INVALID_ARG;
+  const fa_status st = check_split(B, H, Nq, Nk, d, softmax_scale, causal, num_splits, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_part) || !aligned4(lse_part))
+    return FA_ERR_INVALID_ARG;
+  const fa::SplitArgs a{q, k, v, o_part, lse_part, B, H, Nq, Nk, d, softmax_scale, causal,
+                        num_splits, dtype, stream};
+  return fa::launch_splitkv_partial(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                   int num_splits, int rows, int d, int dtype, void* stream) {
+  if (!o_part || !lse_part || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (num_splits < 1 || rows < 1 || d < 1 || d > 1024) return FA_ERR_INVALID_ARG;
+  if (num_splits > kMaxSplits) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) return FA_ERR_UNSUPPORTED;
+  if ((long long)num_splits * rows * d > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  const size_t ea = dtype == FA_DTYPE_FP32 ? 4 : 2;
+  if (!aligned4(o_part) || !aligned4(lse_part) || !aligned4(lse) || ((uintptr_t)o % ea) != 0)
+    return FA_ERR_INVALID_ARG;
+  const fa::MergeArgs a{o_part, lse_part, o, lse, num_splits, rows, d, dtype, stream};
+  return fa::launch_splitkv_merge(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Nq, int Nk, int d, float softmax_scale, int causal,
+                         int num_splits, void* workspace, size_t workspace_bytes, int dtype,
+                         void* stream) {
+  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID_ARG;
+  const fa_status st = check_split(B, H, Nq, Nk, d, softmax_scale, causal, num_splits, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
+      !aligned16(workspace))
+    return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits)) return FA_ERR_INVALID_ARG;
+  float* o_part = (float*)workspace;
+  float* lse_part = (float*)((char*)workspace + split_part_bytes(B, H, Nq, d, num_splits));
+  const fa::SplitArgs a{q, k, v, o_part, lse_part, B, H, Nq, Nk, d, softmax_scale, causal,
+                        num_splits, dtype, stream};
+  if (fa::launch_splitkv_partial(a) != hipSuccess) return FA_ERR_LAUNCH;
+  const fa::MergeArgs m{o_part, lse_part, o, lse, num_splits, B * H * Nq, d, dtype, stream};
+  return fa::launch_splitkv_merge(m) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -37,6 +37,26 @@ struct BwdArgs {
   void* stream;
 };
 
+// Split-KV decoding: partials of every key chunk, then their merge.
+struct SplitArgs {
+  const void *q, *k, *v;
+  float* o_part;    // [nsplit, B, H, Nq, d]
+  float* lse_part;  // [nsplit, B, H, Nq]
+  int B, H, Nq, Nk, d;
+  float scale;
+  int causal, nsplit, dtype;
+  void* stream;
+};
+struct MergeArgs {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int nsplit, rows, d, dtype;
+  void* stream;
+};
+hipError_t launch_splitkv_partial(const SplitArgs& a);
+hipError_t launch_splitkv_merge(const MergeArgs& a);
 hipError_t launch_fwd(const FwdArgs& a);       // dispatches on dtype
 hipError_t launch_fwd_bf16(const FwdArgs& a);  // the gfx950-tuned bf16 kernel
 // Backward stages (fields of BwdArgs a stage does not use may be null).

@@ -14,6 +14,7 @@ import os
 import torch
 
 __all__ = ["lib", "fwd", "bwd", "bwd_stages", "workspace_bytes", "attention", "FaError",
+           "fwd_splitkv", "fwd_partial", "merge", "splitkv_workspace_bytes",
            "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_LAUNCH",
            "FA_DTYPE_BF16", "FA_DTYPE_FP32", "LIB_PATH"]
 
@@ -59,6 +60,14 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_check.restype = i
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_bwd_workspace_bytes.restype = sz
+        L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.fa_splitkv_workspace_bytes.restype = sz
+        L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, i, vp]
+        L.fa_fwd_splitkv.restype = i
+        L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+        L.fa_fwd_partial.restype = i
+        L.fa_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
+        L.fa_merge.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_abi_version.argtypes = []
@@ -162,6 +171,79 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
             raise FaError(r, "fa_bwd_dq")
 
     return [pre, main, dqs]
+
+
+def _check_decode(q, k, v):
+    _check_same(k, v)
+    if q.dim() != 4 or q.dtype != k.dtype or q.device != k.device or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H, Nq, d] tensor of k's dtype and device")
+    B, H, Nq, d = _dims(q)
+    Bk, Hk, Nk, dk = _dims(k)
+    if (Bk, Hk, dk) != (B, H, d):
+        raise ValueError("q [B, H, Nq, d] and k, v [B, H, Nk, d] disagree on B, H or d")
+    return B, H, Nq, Nk, d
+
+
+def splitkv_workspace_bytes(B: int, H: int, Nq: int, d: int, num_splits: int) -> int:
+    return int(lib().fa_splitkv_workspace_bytes(B, H, Nq, d, num_splits))
+
+
+def fwd_splitkv(q, k, v, num_splits: int, scale: float | None = None, causal: bool = False,
+                out=None, lse=None, workspace=None):
+    """Split-KV decoding: O [B,H,Nq,d], lse [B,H,Nq] of q [B,H,Nq,d] over the cache
+    k, v [B,H,Nk,d] cut into ``num_splits`` chunks (partials, then their merge)."""
+    B, H, Nq, Nk, d = _check_decode(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    if workspace is None:
+        n = splitkv_workspace_bytes(B, H, Nq, d, num_splits)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    st = lib().fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
+                              B, H, Nq, Nk, d, float(scale), int(bool(causal)), int(num_splits),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _DTYPES[q.dtype], _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_splitkv")
+    return o, l
+
+
+def fwd_partial(q, k, v, num_splits: int, scale: float | None = None, causal: bool = False,
+                o_part=None, lse_part=None):
+    """First pass of :func:`fwd_splitkv`: float32 o_part [S,B,H,Nq,d], lse_part [S,B,H,Nq]."""
+    B, H, Nq, Nk, d = _check_decode(q, k, v)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    S = int(num_splits)
+    op = torch.empty((S, B, H, Nq, d), dtype=torch.float32, device=q.device) if o_part is None else o_part
+    lp = torch.empty((S, B, H, Nq), dtype=torch.float32, device=q.device) if lse_part is None else lse_part
+    st = lib().fa_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), op.data_ptr(), lp.data_ptr(),
+                              B, H, Nq, Nk, d, float(scale), int(bool(causal)), S,
+                              _DTYPES[q.dtype], _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_partial")
+    return op, lp
+
+
+def merge(o_part, lse_part, dtype: torch.dtype = torch.float32, out=None, lse=None):
+    """Second pass: merge float32 partials o_part [S, ..., d], lse_part [S, ...] into
+    o [..., d] of ``dtype`` and lse [...] float32."""
+    if o_part.dtype != torch.float32 or lse_part.dtype != torch.float32:
+        raise ValueError("partials are float32")
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    if tuple(o_part.shape[:-1]) != tuple(lse_part.shape):
+        raise ValueError("o_part [S, ..., d] and lse_part [S, ...] disagree")
+    S, d = int(o_part.shape[0]), int(o_part.shape[-1])
+    rows = int(lse_part.numel() // max(S, 1))
+    o = torch.empty(tuple(o_part.shape[1:]), dtype=dtype, device=o_part.device) if out is None else out
+    l = torch.empty(tuple(lse_part.shape[1:]), dtype=torch.float32, device=o_part.device) if lse is None else lse
+    st = lib().fa_merge(o_part.data_ptr(), lse_part.data_ptr(), o.data_ptr(), l.data_ptr(),
+                        S, rows, d, _DTYPES[dtype], _stream(o_part.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_merge")
+    return o, l
 
 
 class _Attention(torch.autograd.Function):

@@ -20,7 +20,8 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "to_f64"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "to_f64",
+           "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs"]
 
 
 @dataclass(frozen=True)
@@ -81,6 +82,42 @@ def make_inputs(w: Workload, with_do: bool | None = None) -> dict:
             if b < w.B and h < w.H and row < w.N:
                 x[b, h, row, :] *= np.float32(factor)
         out[name] = _round(x, w.dtype)
+    return out
+
+
+@dataclass(frozen=True)
+class DecodeWorkload:
+    """Nq new query rows per (b, h) against a cache of Nk key/value rows."""
+    name: str
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    dtype: str
+    splits: int
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# Decoding with a long cache at the shape of the pages' split-KV example (batch 4,
+# 16 heads, one new token), head dim 128, cache of 16384 tokens; split into 16
+# chunks (1024 workgroups, four per compute unit).
+DECODE_WORKLOADS = {
+    "decode_long": DecodeWorkload("decode_long", 4, 16, 1, 16384, 128, True, "bf16", 16),
+}
+
+
+def make_decode_inputs(w: DecodeWorkload) -> dict:
+    """Same recipe as make_inputs: q [B,H,Nq,d], then k, v [B,H,Nk,d], drawn in that order."""
+    rng = np.random.default_rng(w.seed)
+    out = {}
+    for name, n in (("q", w.Nq), ("k", w.Nk), ("v", w.Nk)):
+        out[name] = _round(rng.standard_normal((w.B, w.H, n, w.d), dtype=np.float32), w.dtype)
     return out
 
 

@@ -127,6 +127,56 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                     int N, int d, float softmax_scale, int causal, int dtype,
                     void* stream);
 
+/* ---- Split-KV decoding ----------------------------------------------------------
+ * "FlashAttention and online softmax" (Lesson 4), section "Split-KV for decoding
+ * (flash-decoding)": the keys of each row are cut into chunks, each chunk is
+ * reduced to a partial (o, lse) by workgroups of its own, and a second pass merges
+ * the partials of each row with the formula of section "Merging two partial
+ * results": lse = log sum_s e^{lse_s}, o = sum_s e^{lse_s - lse} o_s (an empty
+ * chunk has lse_s = -inf and weight 0).
+ *
+ * A block of Nq query rows per (b, h) -- the newest Nq positions of a sequence whose
+ * key/value cache holds Nk rows -- attends to that cache.
+ *   q : [B, H, Nq, d]; k, v : [B, H, Nk, d]; o : [B, H, Nq, d], all of `dtype`;
+ *   lse : [B, H, Nq] float32.  1 <= Nq <= 8, Nq <= Nk; d 64 or 128.
+ *   causal : 1 = query i (0-based among the Nq) sees key j iff j <= i + (Nk - Nq)
+ *            (for Nq = Nk the rule of fa_fwd; one decoding query sees every key);
+ *            0 = every key.
+ *   num_splits : 1..256 chunks.  With c = ceil(Nk / num_splits), chunk s holds keys
+ *            [s c, min(Nk, (s+1) c)); chunks that start at or past Nk are empty.
+ * Errors: as fa_fwd, plus FA_ERR_INVALID_ARG for Nk < Nq or num_splits < 1 and
+ * FA_ERR_UNSUPPORTED for Nq > 8 (use fa_fwd for many query rows) or
+ * num_splits > 256. */
+
+/* Bytes of workspace fa_fwd_splitkv needs: the float32 partials
+ * o_part [num_splits, B, H, Nq, d] and lse_part [num_splits, B, H, Nq], each region
+ * 256-byte aligned.  0 for invalid sizes. */
+size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits);
+
+/* Both passes (fa_fwd_partial into the workspace, then fa_merge) on one stream. */
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Nq, int Nk, int d, float softmax_scale,
+                         int causal, int num_splits, void* workspace,
+                         size_t workspace_bytes, int dtype, void* stream);
+
+/* First pass: for every chunk s, the attention of each query row over that chunk's
+ * visible keys alone, normalised: o_part[s] (float32, [B, H, Nq, d]) and
+ * lse_part[s] (float32, [B, H, Nq]); a row with no visible key in the chunk gets
+ * o = 0, lse = -inf.  o_part 16-byte aligned, lse_part 4-byte aligned. */
+fa_status fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part,
+                         float* lse_part, int B, int H, int Nq, int Nk, int d,
+                         float softmax_scale, int causal, int num_splits, int dtype,
+                         void* stream);
+
+/* Second pass: merges num_splits partials of `rows` rows of length d
+ * (o_part [num_splits, rows, d] float32, lse_part [num_splits, rows] float32) into
+ * o [rows, d] of `dtype` and lse [rows] float32.  Any order of the chunks gives the
+ * same result up to rounding.  1 <= d <= 1024, 1 <= num_splits <= 256; rows with
+ * every lse_s = -inf get o = 0, lse = -inf.  Pointers need only their element
+ * alignment; INVALID_ARG for null pointers or sizes out of range. */
+fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* lse,
+                   int num_splits, int rows, int d, int dtype, void* stream);
+
 /* Host-only argument checks of fa_fwd / fa_bwd (same rules, same codes); they
  * touch no device and enqueue nothing.  Pointers are checked for null and
  * alignment only. */
