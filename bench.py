@@ -88,6 +88,73 @@ def cpu_baseline(x, w, heads, outs):
         "dK_rel": worst["dK"], "dV_rel": worst["dV"], "heads": len(heads)}
 
 
+def decode_measure(dev, steps: int, warmup: int, cpu: bool):
+    """Split-KV decoding on its workload: HIP-event time of the partial and merge
+    passes, HBM roofline of the partial pass, and the oracle timed beside it."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_14_amd import fa
+    from exact_io_aware_14_amd.accounting import splitkv_bytes
+    from exact_io_aware_14_amd.inputs import DECODE_WORKLOADS, make_decode_inputs, to_f64
+
+    w = DECODE_WORKLOADS["decode_long"]
+    x = make_decode_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    S = w.splits
+    op = torch.empty((S, w.B, w.H, w.Nq, w.d), dtype=torch.float32, device=dev)
+    lp = torch.empty((S, w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+    calls = [lambda: fa.fwd_partial(q, k, v, S, w.scale, w.causal, o_part=op, lse_part=lp),
+             lambda: fa.merge(op, lp, q.dtype, out=o, lse=lse)]
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        calls[0]()
+        e[1].record()
+        calls[1]()
+        e[2].record()
+    torch.cuda.synchronize()
+    wall_us = (time.perf_counter() - t0) * 1e6 / steps
+    part_us = sum(e[0].elapsed_time(e[1]) for e in evs) / steps * 1e3
+    merge_us = sum(e[1].elapsed_time(e[2]) for e in evs) / steps * 1e3
+    b = splitkv_bytes(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, S)
+    achieved = b["partial"] / (part_us * 1e-6) / 1e9
+    rec = {
+        "workload": {"name": w.name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                     "causal": w.causal, "dtype": w.dtype, "splits": S},
+        "partial_us": round(part_us, 2), "merge_us": round(merge_us, 2),
+        "step_us_wall": round(wall_us, 2),
+        "cache_GBps": round((b["partial"] + b["merge"]) / ((part_us + merge_us) * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "splitkv_partial_kernel", "achieved": round(achieved, 1),
+                     "peak": 8000.0, "unit": "GB/s", "frac": round(achieved / 8000.0, 4),
+                     "traffic": measured_traffic("splitkv_partial_kernel", w.name)},
+    }
+    if cpu:
+        from threadpoolctl import threadpool_info
+
+        from oracle import attention_fwd_rect
+
+        Q, K, V = (to_f64(x[n]) for n in ("q", "k", "v"))
+        t1 = time.perf_counter()
+        O_ref, lse_ref = attention_fwd_rect(Q, K, V, w.scale, w.causal)
+        t = time.perf_counter() - t1
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        rec["cpu_baseline"] = {"value": round(b["partial"] / t / 1e9, 3), "unit": "GB/s of cache",
+                               "cores": threads, "kind": "oracle",
+                               "sample": f"the whole workload (all {w.B * w.H} heads), fp64 numpy, {t:.2f} s"}
+        rec["parity_sample"] = {
+            "O_maxabs": float(np.abs(o.float().cpu().numpy() - O_ref).max()),
+            "lse_maxabs": float(np.abs(lse.cpu().numpy() - lse_ref).max())}
+    return rec
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -95,6 +162,7 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--cpu-heads", type=int, default=64, help="heads in the CPU oracle sample (0 = skip)")
+    ap.add_argument("--no-next", action="store_true", help="skip the split-KV decoding measurement")
     ap.add_argument("--traffic-run", action="store_true",
                     help="for rocprofv3 counter passes: a calibration copy, then each kernel once")
     args = ap.parse_args(argv)
@@ -144,6 +212,8 @@ def main(argv=None) -> int:
         torch.neg(src, out=dst)  # calibration: reads and writes COPY_BYTES each
         torch.cuda.synchronize()
         step()
+        torch.cuda.synchronize()
+        decode_measure(dev, 1, 1, False)
         torch.cuda.synchronize()
         print(json.dumps({"traffic_run": w.name, "copy_bytes": COPY_BYTES}), flush=True)
         return 0
@@ -208,6 +278,8 @@ def main(argv=None) -> int:
         rec["parity_sample"] = par
     else:
         rec["cpu_baseline"] = None
+    if not args.no_next:
+        rec["next_rows"] = {"splitkv_decode": decode_measure(dev, args.steps, args.warmup, args.cpu_heads > 0)}
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -7,8 +7,8 @@ Two commands, each a separate rocprofv3 pass (one counter block per pass):
     python -m exact_io_aware_14_amd.traffic <dir> [--workload long_causal]
 
 ``bench.py --traffic-run`` launches, once each after a warm-up: a plain device
-copy of a known size (the calibration kernel), the forward, and the three backward
-stages.  FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch; the copy of
+copy of a known size (the calibration kernel), the forward, the three backward
+stages, and the two split-KV decoding passes on the decoding workload.  FETCH_SIZE and WRITE_SIZE are reported in KiB per dispatch; the copy of
 C bytes must read C and write C bytes, so each counter is scaled by C / (what it
 reads for the copy).  The result, with the hash of the kernel sources it was taken
 on, goes to profiles/traffic.json, which bench.py reads (and ignores once the
@@ -29,12 +29,15 @@ CSRC = os.path.join(ROOT, "exact_io_aware_14_amd", "csrc")
 OUT = os.path.join(ROOT, "profiles", "traffic.json")
 
 COPY_BYTES = 512 << 20  # calibration copy: 512 MiB read + 512 MiB written
-# kernel-name fragments -> names used in bench.py's roofline
+# kernel-name fragments -> (workload the traffic run launches it on, name used in
+# bench.py's roofline)
 KERNELS = {
-    "fwd_bf16_kernel": "fwd_kernel",
-    "bwd_bf16_kernel": "bwd_main_kernel",
-    "bwd_dq_bf16_kernel": "bwd_dq_kernel",
-    "bwd_pre_kernel": "bwd_pre_kernel",
+    "fwd_bf16_kernel": (None, "fwd_kernel"),
+    "bwd_bf16_kernel": (None, "bwd_main_kernel"),
+    "bwd_dq_bf16_kernel": (None, "bwd_dq_kernel"),
+    "bwd_pre_kernel": (None, "bwd_pre_kernel"),
+    "splitkv_partial_kernel": ("decode_long", "splitkv_partial_kernel"),
+    "splitkv_merge_kernel": ("decode_long", "splitkv_merge_kernel"),
 }
 
 
@@ -65,10 +68,11 @@ def read_counter(dirpath: str, counter: str) -> dict:
     return out
 
 
-def classify(name: str) -> str | None:
-    for frag, label in KERNELS.items():
+def classify(name: str):
+    """(workload or None for the main one, label) of a kernel name, or None."""
+    for frag, wl in KERNELS.items():
         if frag in name:
-            return label
+            return wl
     return None
 
 
@@ -85,18 +89,23 @@ def summarize(dirpath: str, workload: str) -> dict:
     w_scale = COPY_BYTES / (copy_kib(write) * 1024.0)
     res = {"source_hash": source_hash(), "copy_bytes": COPY_BYTES,
            "fetch_scale": f_scale, "write_scale": w_scale}
-    kern = {}
-    for label_src, d, scale, key in ((fetch, fetch, f_scale, "fetch_bytes"), (write, write, w_scale, "write_bytes")):
+    out = {"calibration": res}
+    for d, scale, key in ((fetch, f_scale, "fetch_bytes"), (write, w_scale, "write_bytes")):
         for name, vals in d.items():
-            label = classify(name)
-            if label is None:
+            c = classify(name)
+            if c is None:
                 continue
+            wl, label = c
+            kern = out.setdefault(wl or workload, {})
             kern.setdefault(label, {"source_hash": res["source_hash"]})
             kern[label][key] = sum(vals) / len(vals) * 1024.0 * scale
-    for label, e in kern.items():
-        if "fetch_bytes" in e and "write_bytes" in e:
-            e["hbm_bytes_per_launch"] = e["fetch_bytes"] + e["write_bytes"]
-    return {"calibration": res, workload: kern}
+    for wl, kern in out.items():
+        if wl == "calibration":
+            continue
+        for e in kern.values():
+            if "fetch_bytes" in e and "write_bytes" in e:
+                e["hbm_bytes_per_launch"] = e["fetch_bytes"] + e["write_bytes"]
+    return out
 
 
 def main(argv=None) -> int:
