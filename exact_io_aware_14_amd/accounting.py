@@ -80,3 +80,20 @@ def splitkv_bytes(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, num_spli
     part = num_splits * B * H * Nq * (d + 1) * 4
     return {"partial": B * H * (Nq + 2 * Nk) * d * e + part,
             "merge": part + B * H * Nq * (d * e + 4)}
+
+
+def window_pairs(N: int, window: int) -> int:
+    """Visible (query, key) pairs of an N-row causal band of width W (all of the
+    causal triangle for W <= 0): sum over i of min(i + 1, W)."""
+    if window <= 0 or window >= N:
+        return N * (N + 1) // 2
+    return window * (window + 1) // 2 + (N - window) * window
+
+
+def varlen_pairs(lengths, causal: bool, window: int = 0) -> int:
+    """Visible pairs of a packed batch: each sequence attends only within itself."""
+    tot = 0
+    for n in lengths:
+        n = int(n)
+        tot += window_pairs(n, window) if causal else n * n
+    return tot

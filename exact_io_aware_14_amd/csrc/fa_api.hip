@@ -36,6 +36,16 @@ size_t ws_bytes(int B, int H, int N, int d, int dtype) {
   return 2 * vec_bytes(B, H, N) + acc;
 }
 
+// Extra checks of the variable-length / window calls (see fa.h).
+fa_status check_ex(const int* cu, int H, int total, int causal, int window) {
+  if (window < 0 || (window > 0 && causal != 1)) return FA_ERR_INVALID_ARG;
+  if (cu != nullptr) {
+    if (!aligned4(cu) || total < 1) return FA_ERR_INVALID_ARG;
+    if ((long long)H * total > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  }
+  return FA_OK;
+}
+
 // Split-KV decoding sizes (see fa.h).
 constexpr int kMaxSplitRows = 8;
 constexpr int kMaxSplits = 256;
@@ -224,6 +234,40 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
   if (fa::launch_splitkv_partial(a) != hipSuccess) return FA_ERR_LAUNCH;
   const fa::MergeArgs m{o_part, lse_part, o, lse, num_splits, B * H * Nq, d, dtype, stream};
   return fa::launch_splitkv_merge(m) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int B, int H, int N, int total, int d,
+                    float softmax_scale, int causal, int window, int dtype, void* stream) {
+  fa_status st = fa_fwd_check(q, k, v, o, lse, B, H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  st = check_ex(cu_seqlens, H, total, causal, window);
+  if (st != FA_OK) return st;
+  fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, softmax_scale, causal, dtype, stream};
+  a.cu_seqlens = cu_seqlens;
+  a.T = cu_seqlens ? total : 0;
+  a.window = window;
+  return fa::launch_fwd(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, const int* cu_seqlens, int B, int H, int N, int total,
+                    int d, float softmax_scale, int causal, int window, int dtype, void* stream) {
+  fa_status st = fa_bwd_check(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
+                              N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  st = check_ex(cu_seqlens, H, total, causal, window);
+  if (st != FA_OK) return st;
+  fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d, softmax_scale,
+                           causal, dtype, stream);
+  a.cu_seqlens = cu_seqlens;
+  a.T = cu_seqlens ? total : 0;
+  a.window = window;
+  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
 }
 
 }  // extern "C"

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
                                                       float* __restrict__ Dvec,
                                                       float* __restrict__ L2,
                                                       float* __restrict__ dqacc, int N,
-                                                      int Npad, long long prow_total) {
+                                                      int Npad, long long prow_total,
+                                                      SeqMap sm) {
   constexpr int VEC = 16 / sizeof(T);
   constexpr int TPR = D / VEC;  // threads per row (divides 64)
   static_assert(64 % TPR == 0, "a row's threads must sit in one wave");
@@ -49,10 +50,12 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   const int part = (int)(gid % TPR);
   const long long bh = prow / Npad;
   const int q = (int)(prow - bh * Npad);
-  const bool live = prow < prow_total && q < N;
+  int base = 0, len = 0;
+  if (prow < prow_total) seq_rows(sm, (int)bh, N, base, len);
+  const bool live = prow < prow_total && q < len;
   float acc = 0.0f;
   if (live) {
-    const size_t off = (size_t)(bh * N + q) * D + part * VEC;
+    const size_t off = ((size_t)base + q) * D + part * VEC;
     const T* po = O + off;
     const T* pd = dO + off;
 #pragma unroll
@@ -67,25 +70,29 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const T* __restrict__ O,
   for (int o = TPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
   if (prow < prow_total && part == 0) {
     Dvec[prow] = live ? acc : 0.0f;
-    L2[prow] = live ? LSE[bh * N + q] * kLog2e : INFINITY;
+    L2[prow] = live ? LSE[(size_t)base + q] * kLog2e : INFINITY;
   }
 }
 
 // ---------------------------------------------------------------------------
 // 3. dQ = scale * accumulator in the storage dtype (4 elements per thread).  The
-//    accumulator has Npad rows per head; only rows < N are converted.
+//    accumulator has Npad rows per head; only the head's live rows are converted.
 template <typename T>
 __global__ __launch_bounds__(256) void dq_convert_kernel(const float* __restrict__ acc,
                                                          T* __restrict__ dQ, long long n4,
                                                          int N, int Npad, int d4,
-                                                         float scale) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // over B*H*N*d/4
+                                                         float scale, SeqMap sm) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;  // over B*H*Npad*d/4
   if (i >= n4) return;
-  const long long row = i / d4;  // bh * N + q
-  const long long bh = row / N;
-  const long long prow = row + bh * (Npad - N);
-  const float4 v = reinterpret_cast<const float4*>(acc)[prow * d4 + (i - row * d4)];
-  T* p = dQ + i * 4;
+  const long long prow = i / d4;  // bh * Npad + q
+  const long long bh = prow / Npad;
+  const int q = (int)(prow - bh * Npad);
+  int base, len;
+  seq_rows(sm, (int)bh, N, base, len);
+  if (q >= len) return;
+  const long long col4 = i - prow * d4;
+  const float4 v = reinterpret_cast<const float4*>(acc)[i];
+  T* p = dQ + (((size_t)base + q) * d4 + col4) * 4;
   p[0] = from_f32<T>(v.x * scale);
   p[1] = from_f32<T>(v.y * scale);
   p[2] = from_f32<T>(v.z * scale);
@@ -113,8 +120,8 @@ template <typename T, int D, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
-    float* __restrict__ dqacc, T* __restrict__ dK, T* __restrict__ dV, int N, int Npad,
-    float scale, int causal, int nkb) {
+    float* __restrict__ dqacc, T* __restrict__ dK, T* __restrict__ dV, int Nmax, int Npad,
+    float scale, int causal, int nkb, SeqMap sm, int window) {
   using C = BwdCfg<T, D, NW>;
   using M = Mma<T>;
   typedef typename M::op_t op_t;
@@ -135,8 +142,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / nkb;
   const int kb = id - bh * nkb;  // ascending: under a causal mask block 0 has the most work
-  const size_t head = (size_t)bh * N * D;
+  int base, N;  // first row and length of this (batch, head)
+  seq_rows(sm, bh, Nmax, base, N);
+  const size_t head = (size_t)base * D;
   const int k0 = kb * C::BKV;
+  if (k0 >= N) return;  // a short sequence of a variable-length batch: no keys here
   const int kw = k0 + w * 32;  // first key of this wave
   const int mykey = kw + l32;
 
@@ -170,8 +180,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
     dv[dt] = zero16();
   }
   const float c = scale * kLog2e;
-  const int nqt = (N + C::BQ - 1) / C::BQ;
+  int nqt = (N + C::BQ - 1) / C::BQ;
   const int qt0 = causal ? k0 / C::BQ : 0;  // earlier query rows see none of these keys
+  if (window > 0)  // nor do rows past the last key's band
+    nqt = min(nqt, (k0 + C::BKV - 1 + window - 1) / C::BQ + 1);
   const int dq_dt = w % NDT, dq_kp = w / NDT;
   constexpr int KPART = C::BKV / C::NKP;
 
@@ -209,7 +221,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_main_kernel(
     for (int r = 0; r < 16; ++r) {
       const int ql = crow(g, r);
       const int q = qb0 + ql;
-      const bool vis = mykey < N && q < N && (!causal || mykey <= q);
+      const bool vis = mykey < N && q < N && (!causal || mykey <= q) && (window <= 0 || mykey > q - window);
       const float p = vis ? __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse_s[ql])) : 0.0f;
       s[r] = p;
       dp[r] = p * (dp[r] - D_s[ql]);
@@ -269,7 +281,7 @@ static hipError_t launch_pre_cfg(const BwdArgs& a) {
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)a.stream, (const T*)a.o, (const T*)a.dout, a.lse, a.Dvec, a.L2,
-                     a.dqacc, a.N, a.Npad, prows);
+                     a.dqacc, a.N, a.Npad, prows, SeqMap{a.cu_seqlens, a.B, a.T});
   return hipGetLastError();
 }
 
@@ -282,18 +294,18 @@ static hipError_t launch_main_cfg(const BwdArgs& a) {
   hipLaunchKernelGGL((bwd_main_kernel<T, D, NW>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.dout, a.L2, a.Dvec, a.dqacc, (T*)a.dk, (T*)a.dv, a.N, a.Npad,
-                     a.scale, a.causal, nkb);
+                     a.scale, a.causal, nkb, SeqMap{a.cu_seqlens, a.B, a.T}, a.window);
   return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_fin_cfg(const BwdArgs& a) {
-  const long long n4 = (long long)a.B * a.H * a.N * a.d / 4;
+  const long long n4 = (long long)a.B * a.H * a.Npad * a.d / 4;
   const long long blocks = (n4 + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)a.stream, a.dqacc, (T*)a.dq, n4, a.N, a.Npad, a.d / 4,
-                     a.scale);
+                     a.scale, SeqMap{a.cu_seqlens, a.B, a.T});
   return hipGetLastError();
 }
 

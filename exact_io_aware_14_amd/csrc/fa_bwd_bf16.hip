@@ -71,12 +71,15 @@ __device__ __forceinline__ bf16x8_t tr_pair(const __bf16* lo, const __bf16* hi) 
   return r;
 }
 
-template <int D>
+template <int D, bool GEN>
 __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int Npad, float scale, int causal,
-    int nkb) {
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int Nmax, int Npad, float scale, int causal,
+    int nkb, SeqMap sm_arg, int window_arg) {
+  // GEN = false: dense tensors, no window; the general code folds away.
+  const int window = GEN ? window_arg : 0;
+  const SeqMap sm{GEN ? sm_arg.cu : nullptr, sm_arg.B, sm_arg.T};
   using C = BwdFast<D>;
   constexpr int NKK = D / 16;
   constexpr int NDT = C::NDT;
@@ -100,9 +103,12 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / nkb;
   const int kb = id - bh * nkb;
-  const size_t head = (size_t)bh * N * D;
+  int base, N;  // first row and length of this (batch, head)
+  seq_rows(sm, bh, Nmax, base, N);
+  const size_t head = (size_t)base * D;
   const size_t hpad = (size_t)bh * Npad;
   const int k0 = kb * C::BKV;
+  if (k0 >= N) return;  // a short sequence of a variable-length batch: no keys here
   const int kw = k0 + w * 32;
   const int mykey = kw + l32;
 
@@ -173,8 +179,11 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     dv[dt] = zero16();
   }
   const float c = scale * kLog2e;
-  const int nqt = Npad / C::BQ;
-  const int qt0 = causal ? k0 / C::BQ : 0;  // earlier query rows see none of these keys
+  // query tiles of this sequence (its padded rows hold lse = +inf: P = 0 there) ...
+  int nqt = (N + C::BQ - 1) / C::BQ;
+  const int qt0 = causal ? k0 / C::BQ : 0;  // ... earlier rows see none of these keys
+  if (window > 0)  // ... nor do rows past the last key's band
+    nqt = min(nqt, (k0 + C::BKV - 1 + window - 1) / C::BQ + 1);
 
   // P^T and dS^T of the previous tile, as bf16 A operands (j = 0, 1 query halves).
   // They start at zero, so the first step's dV/dK products add nothing.
@@ -227,10 +236,11 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
 
     // Keys past the end and, on tiles crossing the diagonal, keys above it: S = -inf,
     // so P = 2^-inf = 0 and dS = 0.  Only those tiles pay for the per-element test.
-    if ((kw + 32 > N) || (causal && kw + 31 > qb0)) {
+    if ((kw + 32 > N) || (causal && kw + 31 > qb0) || (window > 0 && qb0 + 31 >= kw + window)) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const bool dead = (mykey >= N) | (causal & (mykey > qb0 + crow(g, r)));
+        const int q = qb0 + crow(g, r);
+        const bool dead = (mykey >= N) | (causal & (mykey > q)) | ((window > 0) & (q - mykey >= window));
         s[r] = dead ? -INFINITY : s[r];
       }
     }
@@ -321,22 +331,24 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     }
 }
 
-template <int D>
+template <int D, bool GEN>
 static hipError_t launch_bwd_bf16_d(const BwdArgs& a) {
   using C = BwdFast<D>;
   const int nkb = (a.N + C::BKV - 1) / C::BKV;
   const long long grid = (long long)a.B * a.H * nkb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_bf16_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0,
+  hipLaunchKernelGGL((bwd_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dk,
-                     (__bf16*)a.dv, a.N, a.Npad, a.scale, a.causal, nkb);
+                     (__bf16*)a.dv, a.N, a.Npad, a.scale, a.causal, nkb,
+                     SeqMap{a.cu_seqlens, a.B, a.T}, a.window);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_main_bf16(const BwdArgs& a) {
-  if (a.d == 64) return launch_bwd_bf16_d<64>(a);
-  if (a.d == 128) return launch_bwd_bf16_d<128>(a);
+  const bool gen = a.cu_seqlens != nullptr || a.window > 0;
+  if (a.d == 64) return gen ? launch_bwd_bf16_d<64, true>(a) : launch_bwd_bf16_d<64, false>(a);
+  if (a.d == 128) return gen ? launch_bwd_bf16_d<128, true>(a) : launch_bwd_bf16_d<128, false>(a);
   return hipErrorInvalidValue;
 }
 

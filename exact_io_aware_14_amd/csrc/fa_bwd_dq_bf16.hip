@@ -47,11 +47,15 @@ __device__ __forceinline__ void dq_dma16(const void* g, void* lds_wave_base) {
                                    (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
 }
 
-template <int D>
+template <int D, bool GEN>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
-    __bf16* __restrict__ dQ, int N, int Npad, float scale, int causal, int nqb) {
+    __bf16* __restrict__ dQ, int Nmax, int Npad, float scale, int causal, int nqb, SeqMap sm_arg,
+    int window_arg) {
+  // GEN = false: dense tensors, no window; the general code folds away.
+  const int window = GEN ? window_arg : 0;
+  const SeqMap sm{GEN ? sm_arg.cu : nullptr, sm_arg.B, sm_arg.T};
   using C = DqFast<D>;
   constexpr int NKK = D / 16;
   constexpr int NDT = D / 32;
@@ -68,8 +72,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int bh = id / nqb;
   int qb = id - bh * nqb;
   if (causal) qb = nqb - 1 - qb;  // longest query blocks of a head first
-  const size_t head = (size_t)bh * N * D;
+  int base, N;  // first row and length of this (batch, head)
+  seq_rows(sm, bh, Nmax, base, N);
+  const size_t head = (size_t)base * D;
   const int q0 = qb * C::BR;
+  if (q0 >= N) return;  // a short sequence of a variable-length batch: no rows here
   const int qw = q0 + w * 32;
   const int myq = qw + l32;
 
@@ -139,10 +146,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     if (kt + 1 < nkt) issue_tile(kt + 1, Kn, Vn);
     const int k0 = kt * C::BC;
     if (causal && k0 > qw + 31) return;  // tile wholly above this wave's rows
+    if (window > 0 && k0 + C::BC - 1 <= qw - window) return;  // wholly below their band
 
     // The tile's two 32-key halves one after the other: half 1's products can run
     // while half 0's P and dS are computed, and only one half's S and dP are live.
-    const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw);
+    const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw) ||
+                           (window > 0 && k0 <= qw + 31 - window);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       f32x16_t s = zero16(), dp = zero16();
@@ -157,7 +166,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + ks * 32 + crow(g, r);
-          s[r] = ((key >= N) | (causal & (key > myq))) ? -INFINITY : s[r];
+          s[r] = ((key >= N) | (causal & (key > myq)) | ((window > 0) & (key <= myq - window))) ? -INFINITY : s[r];
         }
       }
 #pragma unroll
@@ -191,8 +200,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     }
   };
 
-  issue_tile(0, K0, V0);
-  for (int kt = 0; kt < nkt; kt += 2) {
+  // first key tile of the block's band (sliding window), else tile 0
+  const int kt0 = window > 0 ? max(0, q0 - window + 1) / C::BC : 0;
+  issue_tile(kt0, K0, V0);
+  for (int kt = kt0; kt < nkt; kt += 2) {
     tile(kt, K0, V0, K1, V1);
     if (kt + 1 < nkt) tile(kt + 1, K1, V1, K0, V0);
   }
@@ -212,22 +223,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   }
 }
 
-template <int D>
+template <int D, bool GEN>
 static hipError_t launch_dq_bf16_d(const BwdArgs& a) {
   using C = DqFast<D>;
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const long long grid = (long long)a.B * a.H * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dq,
-                     a.N, a.Npad, a.scale, a.causal, nqb);
+                     a.N, a.Npad, a.scale, a.causal, nqb, SeqMap{a.cu_seqlens, a.B, a.T},
+                     a.window);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
-  if (a.d == 64) return launch_dq_bf16_d<64>(a);
-  if (a.d == 128) return launch_dq_bf16_d<128>(a);
+  const bool gen = a.cu_seqlens != nullptr || a.window > 0;
+  if (a.d == 64) return gen ? launch_dq_bf16_d<64, true>(a) : launch_dq_bf16_d<64, false>(a);
+  if (a.d == 128) return gen ? launch_dq_bf16_d<128, true>(a) : launch_dq_bf16_d<128, false>(a);
   return hipErrorInvalidValue;
 }
 

@@ -113,6 +113,31 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
   return (id % kXcd) * (n / kXcd) + id / kXcd;
 }
 
+// Rows of one (batch, head) unit of work.  Dense: [B, H, N, d], unit bh = b*H + h
+// owns rows bh*N .. bh*N + N-1.  Variable length (cu != null): tensors are packed
+// head-major [H, T, d] with sequence b in rows cu[b] .. cu[b+1]-1 of every head, and
+// unit bh = h*B + b owns rows h*T + cu[b] ...  The boundaries are device data the
+// host cannot see: they are clamped to 0 <= cu[b] <= cu[b+1] <= T and the length to
+// Nmax, so that a malformed table can give wrong rows but never an access outside
+// the tensors.
+struct SeqMap {
+  const int* cu;  // null: dense
+  int B;          // sequences (varlen)
+  int T;          // rows per head (varlen)
+};
+__device__ __forceinline__ void seq_rows(const SeqMap& m, int bh, int Nmax, int& base, int& len) {
+  if (m.cu == nullptr) {
+    base = bh * Nmax;
+    len = Nmax;
+    return;
+  }
+  const int h = bh / m.B, b = bh - h * m.B;
+  const int c0 = min(max(m.cu[b], 0), m.T);
+  const int c1 = min(max(m.cu[b + 1], c0), m.T);
+  base = h * m.T + c0;
+  len = min(c1 - c0, Nmax);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 // Start value of the running max: finite, so that exp2((m_old - m_new) * c) and
 // s * c - m * c never form -inf - (-inf) while a row has seen no visible key.

@@ -54,7 +54,8 @@ __device__ __forceinline__ void store4<__bf16>(__bf16* p, float a, float b, floa
 template <typename T, int D, int BC, int NW, int QT>
 __global__ __launch_bounds__(64 * NW) void fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    T* __restrict__ O, float* __restrict__ LSE, int N, float scale, int causal, int nqb) {
+    T* __restrict__ O, float* __restrict__ LSE, int Nmax, float scale, int causal, int nqb,
+    SeqMap sm, int window) {
   using C = FwdCfg<T, D, BC, NW, QT>;
   using M = Mma<T>;
   typedef typename M::op_t op_t;
@@ -73,11 +74,14 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
   const int bh = id / nqb;
   int qb = id - bh * nqb;
   if (causal) qb = nqb - 1 - qb;  // longest query blocks of a head start first
-  const size_t head = (size_t)bh * N * D;
+  int base, N;  // first row and length of this (batch, head)
+  seq_rows(sm, bh, Nmax, base, N);
+  const size_t head = (size_t)base * D;
   const T* Qh = Q + head;
   const T* Kh = K + head;
   const T* Vh = V + head;
   const int q0 = qb * C::BR;
+  if (q0 >= N) return;  // a short sequence of a variable-length batch: no rows here
   const int qw = q0 + w * 32 * QT;  // first query row of this wave
 
   // Q^T as the B operand of S^T = K Q^T (natural k assignment), kept in registers.
@@ -130,8 +134,10 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
     }
   };
 
-  gload(0);
-  for (int kt = 0; kt < nkt; ++kt) {
+  // first key tile of the block's band (sliding window), else tile 0
+  const int kt0 = window > 0 ? max(0, q0 - window + 1) / BC : 0;
+  gload(kt0);
+  for (int kt = kt0; kt < nkt; ++kt) {
     __syncthreads();  // every wave is done reading the previous tile
     sstore();
     __syncthreads();
@@ -157,7 +163,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
 
     // Mask keys past the end and, on tiles that reach past this wave's first
     // query, keys above the diagonal.
-    const bool need_mask = (k0 + BC > N) || (causal && k0 + BC - 1 > qw);
+    const bool need_mask = (k0 + BC > N) || (causal && k0 + BC - 1 > qw) ||
+                           (window > 0 && k0 <= qw + 32 * QT - 1 - window);
     if (need_mask) {
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
@@ -167,7 +174,8 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + ks * 32 + crow(g, r);
-            if (key >= N || (causal && key > q)) s[ks][qt][r] = -INFINITY;
+            if (key >= N || (causal && key > q) || (window > 0 && key <= q - window))
+              s[ks][qt][r] = -INFINITY;
           }
         }
     }
@@ -234,7 +242,7 @@ __global__ __launch_bounds__(64 * NW) void fwd_kernel(
                     a[4 * rb + 2] * inv, a[4 * rb + 3] * inv);
         }
       if (g == 0)
-        LSE[(size_t)bh * N + q] = l_tot > 0.0f ? fmaf(mrun[qt], scale, logf(l_tot)) : -INFINITY;
+        LSE[(size_t)base + q] = l_tot > 0.0f ? fmaf(mrun[qt], scale, logf(l_tot)) : -INFINITY;
     }
   }
 }
@@ -247,7 +255,8 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, QT>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
-                     (T*)a.o, a.lse, a.N, a.scale, a.causal, nqb);
+                     (T*)a.o, a.lse, a.N, a.scale, a.causal, nqb, SeqMap{a.cu_seqlens, a.B, a.T},
+                     a.window);
   return hipGetLastError();
 }
 

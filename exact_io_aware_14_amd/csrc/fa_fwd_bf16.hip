@@ -63,10 +63,14 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
                                    (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
 }
 
-template <int D>
+template <int D, bool GEN>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int N, float scale, int causal, int nqb) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int Nmax, float scale, int causal, int nqb,
+    SeqMap sm_arg, int window_arg) {
+  // GEN = false: dense tensors, no window; the general code folds away.
+  const int window = GEN ? window_arg : 0;
+  const SeqMap sm{GEN ? sm_arg.cu : nullptr, sm_arg.B, sm_arg.T};
   using C = FwdFast<D>;
   constexpr int NKK = D / 16;  // MFMA steps along d
   constexpr int NDT = D / 32;  // 32-wide dim tiles of O^T
@@ -86,10 +90,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
   const int bh = id / nqb;
   int qb = id - bh * nqb;
   if (causal) qb = nqb - 1 - qb;
-  const size_t head = (size_t)bh * N * D;
+  int base, N;  // first row and length of this (batch, head)
+  seq_rows(sm, bh, Nmax, base, N);
+  const size_t head = (size_t)base * D;
   const __bf16* Kh = K + head;
   const __bf16* Vh = V + head;
   const int q0 = qb * C::BR;
+  if (q0 >= N) return;  // a short sequence of a variable-length batch: no rows here
   const int qw = q0 + w * 32;
   const int myq = qw + l32;
 
@@ -163,6 +170,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     if (kt + 1 < nkt) issue_tile(kt + 1, Kn, Vn);
     const int k0 = kt * C::BC;
     if (causal && k0 > qw + 31) return;  // tile wholly above this wave's rows
+    if (window > 0 && k0 + C::BC - 1 <= qw - window) return;  // wholly below their band
     // S^T = K Q^T
     f32x16_t s[2];
     s[0] = zero16();
@@ -176,14 +184,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], s[ks], 0, 0, 0);
       }
 
-    const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw);
+    const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw) ||
+                           (window > 0 && k0 <= qw + 31 - window);
     if (need_mask) {
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + ks * 32 + crow(g, r);
-          if (key >= N || (causal && key > myq)) s[ks][r] = -INFINITY;
+          if (key >= N || (causal && key > myq) || (window > 0 && key <= myq - window))
+            s[ks][r] = -INFINITY;
         }
     }
 
@@ -245,8 +255,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
       }
   };
 
-  issue_tile(0, K0, V0);
-  for (int kt = 0; kt < nkt; kt += 2) {
+  // first key tile of the block's band (sliding window), else tile 0
+  const int kt0 = window > 0 ? max(0, q0 - window + 1) / C::BC : 0;
+  issue_tile(kt0, K0, V0);
+  for (int kt = kt0; kt < nkt; kt += 2) {
     tile(kt, K0, V0, K1, V1);
     if (kt + 1 < nkt) tile(kt + 1, K1, V1, K0, V0);
   }
@@ -266,25 +278,27 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         for (int t = 0; t < 4; ++t) v[t] = (__bf16)(oacc[dt][4 * rb + t] * inv);
         *reinterpret_cast<bf16x4_t*>(orow + dt * 32 + 8 * rb + 4 * g) = v;
       }
-    if (g == 0) LSE[(size_t)bh * N + myq] = l_tot > 0.0f ? fmaf(mref, scale, logf(l_tot)) : -INFINITY;
+    if (g == 0) LSE[(size_t)base + myq] = l_tot > 0.0f ? fmaf(mref, scale, logf(l_tot)) : -INFINITY;
   }
 }
 
-template <int D>
+template <int D, bool GEN>
 static hipError_t launch_fwd_bf16_d(const FwdArgs& a) {
   using C = FwdFast<D>;
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const long long grid = (long long)a.B * a.H * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D>), dim3((unsigned)grid), dim3(C::NT), 0,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
-                     (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.N, a.scale, a.causal, nqb);
+                     (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.N, a.scale, a.causal, nqb,
+                     SeqMap{a.cu_seqlens, a.B, a.T}, a.window);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a) {
-  if (a.d == 64) return launch_fwd_bf16_d<64>(a);
-  if (a.d == 128) return launch_fwd_bf16_d<128>(a);
+  const bool gen = a.cu_seqlens != nullptr || a.window > 0;
+  if (a.d == 64) return gen ? launch_fwd_bf16_d<64, true>(a) : launch_fwd_bf16_d<64, false>(a);
+  if (a.d == 128) return gen ? launch_fwd_bf16_d<128, true>(a) : launch_fwd_bf16_d<128, false>(a);
   return hipErrorInvalidValue;
 }
 

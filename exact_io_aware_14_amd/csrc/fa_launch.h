@@ -13,6 +13,9 @@ enum { kBF16 = 0, kFP32 = 1 };
 constexpr int kRowPad = 32;
 inline int pad_rows(int N) { return (N + kRowPad - 1) / kRowPad * kRowPad; }
 
+// Dense calls: cu_seqlens = null, N the sequence length.  Variable-length calls:
+// cu_seqlens = B+1 device boundaries, tensors packed [H, T, d], N the longest length.
+// window > 0: causal band, query i sees key j iff i - window < j <= i.
 struct FwdArgs {
   const void *q, *k, *v;
   void* o;
@@ -21,6 +24,9 @@ struct FwdArgs {
   float scale;
   int causal, dtype;
   void* stream;
+  const int* cu_seqlens = nullptr;
+  int T = 0;
+  int window = 0;
 };
 
 struct BwdArgs {
@@ -35,6 +41,9 @@ struct BwdArgs {
   float scale;
   int causal, dtype;
   void* stream;
+  const int* cu_seqlens = nullptr;
+  int T = 0;
+  int window = 0;
 };
 
 // Split-KV decoding: partials of every key chunk, then their merge.

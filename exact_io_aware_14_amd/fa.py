@@ -14,7 +14,7 @@ import os
 import torch
 
 __all__ = ["lib", "fwd", "bwd", "bwd_stages", "workspace_bytes", "attention", "FaError",
-           "fwd_splitkv", "fwd_partial", "merge", "splitkv_workspace_bytes",
+           "fwd_splitkv", "fwd_partial", "merge", "splitkv_workspace_bytes", "fwd_ex", "bwd_ex",
            "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_LAUNCH",
            "FA_DTYPE_BF16", "FA_DTYPE_FP32", "LIB_PATH"]
 
@@ -60,6 +60,11 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_check.restype = i
         L.fa_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_bwd_workspace_bytes.restype = sz
+        L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+        L.fa_fwd_ex.restype = i
+        L.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, i,
+                                i, vp]
+        L.fa_bwd_ex.restype = i
         L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_splitkv_workspace_bytes.restype = sz
         L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, i, vp]
@@ -171,6 +176,65 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
             raise FaError(r, "fa_bwd_dq")
 
     return [pre, main, dqs]
+
+
+def _ex_dims(q, cu_seqlens, max_seqlen):
+    """(B, H, N, total, d, lse shape, cu pointer) of a dense or packed call."""
+    if cu_seqlens is None:
+        B, H, N, d = _dims(q)
+        return B, H, N, 0, d, (B, H, N), 0
+    if q.dim() != 3:
+        raise ValueError("variable-length tensors are packed [H, total, d]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.device != q.device \
+            or not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous int32 [B+1] tensor on q's device")
+    if max_seqlen is None:
+        raise ValueError("max_seqlen is required with cu_seqlens")
+    H, T, d = (int(x) for x in q.shape)
+    return int(cu_seqlens.numel()) - 1, H, int(max_seqlen), T, d, (H, T), cu_seqlens.data_ptr()
+
+
+def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0,
+           cu_seqlens=None, max_seqlen: int | None = None, out=None, lse=None):
+    """Forward with a sliding window and/or variable-length packed sequences
+    ([H, total, d] with int32 cu_seqlens [B+1]); see fa_fwd_ex in include/fa.h."""
+    _check_same(q, k, v)
+    B, H, N, T, d, lshape, cu = _ex_dims(q, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    l = torch.empty(lshape, dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), cu,
+                         B, H, N, T, d, float(scale), int(bool(causal)), int(window),
+                         _DTYPES[q.dtype], _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_fwd_ex")
+    return o, l
+
+
+def bwd_ex(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False, window: int = 0,
+           cu_seqlens=None, max_seqlen: int | None = None, workspace=None, grads=None):
+    """Backward of :func:`fwd_ex` (same layout and arguments)."""
+    _check_same(q, k, v, o, do)
+    B, H, N, T, d, lshape, cu = _ex_dims(q, cu_seqlens, max_seqlen)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != lshape or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 {lshape} tensor")
+    if workspace is None:
+        workspace = torch.empty(max(workspace_bytes(B, H, N, d, q.dtype), 1), dtype=torch.uint8,
+                                device=q.device)
+    if grads is None:
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = grads
+    st = lib().fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(), cu,
+                         B, H, N, T, d, float(scale), int(bool(causal)), int(window),
+                         _DTYPES[q.dtype], _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_ex")
+    return dq, dk, dv
 
 
 def _check_decode(q, k, v):

@@ -21,7 +21,9 @@ import numpy as np
 import torch
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "to_f64",
-           "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs"]
+           "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs",
+           "WINDOW_WORKLOADS", "VarlenWorkload", "VARLEN_WORKLOADS", "varlen_lengths",
+           "make_varlen_inputs"]
 
 
 @dataclass(frozen=True)
@@ -118,6 +120,57 @@ def make_decode_inputs(w: DecodeWorkload) -> dict:
     out = {}
     for name, n in (("q", w.Nq), ("k", w.Nk), ("v", w.Nk)):
         out[name] = _round(rng.standard_normal((w.B, w.H, n, w.d), dtype=np.float32), w.dtype)
+    return out
+
+
+# Long-context training with a sliding window: the long-context shape (1 x 16 heads,
+# N = 16384, d = 128, causal) with a band of 4096 keys.
+WINDOW_WORKLOADS = {
+    "window_long": (Workload("window_long", 1, 16, 16384, 128, True, "bf16", True), 4096),
+}
+
+
+@dataclass(frozen=True)
+class VarlenWorkload:
+    """A batch of `n_seqs` sequences packed head-major [H, T, d], lengths drawn
+    log-uniform in [min_len, max_len] (rounded)."""
+    name: str
+    n_seqs: int
+    min_len: int
+    max_len: int
+    H: int
+    d: int
+    causal: bool
+    dtype: str
+    seed: int = 0
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+VARLEN_WORKLOADS = {
+    "varlen_mix": VarlenWorkload("varlen_mix", 16, 256, 4096, 16, 128, True, "bf16"),
+}
+
+
+def varlen_lengths(w: VarlenWorkload) -> np.ndarray:
+    """Sequence lengths: rng = default_rng(seed + 1); exp(uniform(log min, log max)),
+    rounded to integers."""
+    rng = np.random.default_rng(w.seed + 1)
+    x = rng.uniform(math.log(w.min_len), math.log(w.max_len), size=w.n_seqs)
+    return np.rint(np.exp(x)).astype(np.int64)
+
+
+def make_varlen_inputs(w: VarlenWorkload, lengths=None, with_do: bool = True) -> dict:
+    """q, k, v[, do] packed [H, T, d] and cu_seqlens (int32, [B+1]); the draws follow
+    make_inputs' recipe with shape (H, T, d)."""
+    lens = varlen_lengths(w) if lengths is None else np.asarray(lengths, dtype=np.int64)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rng = np.random.default_rng(w.seed)
+    out = {"cu": torch.from_numpy(cu), "max_len": int(lens.max()) if len(lens) else 0}
+    for name in ["q", "k", "v"] + (["do"] if with_do else []):
+        out[name] = _round(rng.standard_normal((w.H, int(cu[-1]), w.d), dtype=np.float32), w.dtype)
     return out
 
 

@@ -127,6 +127,35 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                     int N, int d, float softmax_scale, int causal, int dtype,
                     void* stream);
 
+/* ---- Variable-length batches and sliding windows ---------------------------------
+ * fa_fwd_ex / fa_bwd_ex take the arguments of fa_fwd / fa_bwd plus:
+ *   cu_seqlens : NULL for dense [B, H, N, d] tensors (then `total` is ignored and
+ *       the calls equal fa_fwd / fa_bwd with the window below).  Otherwise B+1 int32
+ *       values in device memory, 0 = cu[0] <= cu[1] <= ... <= cu[B] = total: a batch
+ *       of B sequences of lengths cu[b+1] - cu[b] (zero allowed) packed without
+ *       padding ("FlashAttention from Scratch", "Pitfalls that turn into incidents":
+ *       pass cu_seqlens instead of padded batches).  Tensors are then packed
+ *       head-major, [H, total, d] (sequence b of head h in rows cu[b] .. cu[b+1]-1),
+ *       lse is [H, total] float32, N is the longest length (max_seqlen) and every
+ *       sequence attends only within itself.  The table is read on the device and not
+ *       checked: a table outside these rules gives undefined rows (it can never make a
+ *       kernel access memory outside the tensors) and lengths above N are cut to N.
+ *   window : 0 = no window.  W >= 1 (requires causal = 1): a causal band, query i
+ *       sees key j iff i - W < j <= i ("FlashAttention and online softmax", "Where it
+ *       shows up": sliding-window masks with tile skipping); tiles outside the band
+ *       are skipped.
+ * fa_bwd_ex's workspace: fa_bwd_workspace_bytes(B, H, N, d, dtype), N = max_seqlen.
+ * Errors: as fa_fwd / fa_bwd, plus FA_ERR_INVALID_ARG for window < 0, window > 0
+ * with causal = 0, a misaligned cu_seqlens, total < 1 or H * total >= 2^31. */
+fa_status fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens, int B, int H, int N, int total, int d,
+                    float softmax_scale, int causal, int window, int dtype, void* stream);
+fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, const int* cu_seqlens, int B,
+                    int H, int N, int total, int d, float softmax_scale, int causal,
+                    int window, int dtype, void* stream);
+
 /* ---- Split-KV decoding ----------------------------------------------------------
  * "FlashAttention and online softmax" (Lesson 4), section "Split-KV for decoding
  * (flash-decoding)": the keys of each row are cut into chunks, each chunk is

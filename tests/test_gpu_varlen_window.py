@@ -1,0 +1,179 @@
+"""GPU parity of the sliding window and of variable-length batches (fa_fwd_ex /
+fa_bwd_ex) against the CPU fp64 oracle (oracle/varlen.py, oracle/attention.py).
+
+Bars as for fa_fwd / fa_bwd (tests/parity.py).  Extra properties: with equal
+lengths the packed path returns bit for bit what the dense path returns, and a
+window of W >= N returns bit for bit the plain causal result.
+"""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_14_amd import fa
+from exact_io_aware_14_amd.inputs import (VARLEN_WORKLOADS, WINDOW_WORKLOADS, VarlenWorkload,
+                                          Workload, make_inputs, make_varlen_inputs, to_f64)
+from oracle import attention_bwd, attention_fwd
+from oracle.varlen import varlen_bwd, varlen_fwd, window_mask
+from parity import check_fwd, check_grad
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    fa.lib()
+    return torch.device("cuda:0")
+
+
+def run_dense_window(x, w, window, dev):
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((w.B, w.H, w.N), float("nan"), device=dev)
+    fa.fwd_ex(q, k, v, w.scale, True, window, out=o, lse=lse)
+    nb = fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=dev)
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    fa.bwd_ex(q, k, v, o, do, lse, w.scale, True, window, workspace=ws, grads=grads)
+    torch.cuda.synchronize()
+    return o, lse, grads
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("shape,window", [((1, 1, 300), 1), ((1, 1, 300), 7), ((2, 2, 1000), 100),
+                                          ((1, 2, 1000), 300), ((1, 1, 513), 64), ((2, 1, 129), 1000)],
+                         ids=lambda v: str(v))
+def test_window_small(dev, dtype, d, shape, window):
+    B, H, N = shape
+    w = Workload("win", B, H, N, d, True, dtype, True, seed=N + window + d)
+    say(f"[window] {dtype} B={B} H={H} N={N} d={d} W={window}")
+    x = make_inputs(w)
+    o, lse, (dq, dk, dv) = run_dense_window(x, w, window, dev)
+    Q, K, V, dO = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    m = window_mask(N, window)
+    O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, True, mask=m)
+    check_fwd(dtype, o.cpu(), lse.cpu(), O_ref, lse_ref, "window fwd")
+    g_ref = attention_bwd(Q, K, V, dO, w.scale, True, mask=m)
+    for name, g, r in zip(("dQ", "dK", "dV"), (dq, dk, dv), g_ref):
+        check_grad(dtype, g.cpu(), r, f"window {name}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_wide_window_is_causal_bitwise(dev, dtype):
+    w = Workload("wide", 1, 2, 700, 64, True, dtype, True, seed=3)
+    x = make_inputs(w)
+    q, k, v = (x[n].to(dev) for n in ("q", "k", "v"))
+    o1, l1 = fa.fwd(q, k, v, w.scale, True)
+    o2, l2 = fa.fwd_ex(q, k, v, w.scale, True, window=700)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+LENS = [[1], [300, 1000, 77], [0, 5, 0, 129, 64], [1000, 1000], [33, 2049, 1, 700]]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(False, 0), (True, 0), (True, 50)])
+@pytest.mark.parametrize("lens", LENS, ids=lambda l: "L" + "-".join(map(str, l)))
+def test_varlen_small(dev, dtype, d, causal, window, lens):
+    w = VarlenWorkload("vl", len(lens), 1, 1, 2, d, causal, dtype, seed=sum(lens) + d)
+    say(f"[varlen] {dtype} d={d} causal={causal} W={window} lens={lens}")
+    x = make_varlen_inputs(w, lengths=lens)
+    cu = x["cu"].to(dev)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    H, T = q.shape[0], q.shape[1]
+    nmax = max(1, x["max_len"])
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((H, T), float("nan"), device=dev)
+    fa.fwd_ex(q, k, v, w.scale, causal, window, cu_seqlens=cu, max_seqlen=nmax, out=o, lse=lse)
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    ws = torch.full((fa.workspace_bytes(len(lens), H, nmax, d, q.dtype),), 0xFF, dtype=torch.uint8,
+                    device=dev)
+    fa.bwd_ex(q, k, v, o, do, lse, w.scale, causal, window, cu_seqlens=cu, max_seqlen=nmax,
+              workspace=ws, grads=grads)
+    torch.cuda.synchronize()
+    Q, K, V, dO = (to_f64(x[n]) for n in ("q", "k", "v", "do"))
+    cuh = x["cu"].numpy()
+    O_ref, lse_ref = varlen_fwd(Q, K, V, cuh, w.scale, causal, window)
+    check_fwd(dtype, o.cpu(), lse.cpu(), O_ref, lse_ref, "varlen fwd")
+    g_ref = varlen_bwd(Q, K, V, dO, cuh, w.scale, causal, window)
+    for name, g, r in zip(("dQ", "dK", "dV"), grads, g_ref):
+        check_grad(dtype, g.cpu(), r, f"varlen {name}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_bitwise_dense(dev, causal):
+    """Packed with equal lengths == dense, bit for bit (same kernels, same order)."""
+    B, H, N, d = 3, 2, 384, 128
+    w = Workload("eq", B, H, N, d, causal, "bf16", True, seed=9)
+    x = make_inputs(w)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, w.scale, causal)
+    g = fa.bwd(q, k, v, o, do, lse, w.scale, causal)
+    pk = lambda t: t.permute(1, 0, 2, 3).reshape(H, B * N, d).contiguous()
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device=dev)
+    ov, lv = fa.fwd_ex(pk(q), pk(k), pk(v), w.scale, causal, cu_seqlens=cu, max_seqlen=N)
+    gv = fa.bwd_ex(pk(q), pk(k), pk(v), ov, pk(do), lv, w.scale, causal, cu_seqlens=cu, max_seqlen=N)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, pk(o))
+    assert torch.equal(lv, lse.permute(1, 0, 2).reshape(H, B * N))
+    for a, b in zip(gv, g):
+        assert torch.equal(a, pk(b))
+
+
+def test_window_long_full_size(dev):
+    """The long-context shape with a 4096-key window, two whole heads against the oracle."""
+    w, window = WINDOW_WORKLOADS["window_long"]
+    say(f"[window_long] N={w.N} W={window}")
+    x = make_inputs(w)
+    o, lse, grads = run_dense_window(x, w, window, dev)
+    m = window_mask(w.N, window)
+    for h in (0, w.H - 1):
+        sl = lambda t: to_f64(t[:, h:h + 1])
+        Q, K, V, dO = (sl(x[n]) for n in ("q", "k", "v", "do"))
+        O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, True, mask=m)
+        check_fwd(w.dtype, o[:, h:h + 1].cpu(), lse[:, h:h + 1].cpu(), O_ref, lse_ref, f"head {h}")
+        g_ref = attention_bwd(Q, K, V, dO, w.scale, True, mask=m)
+        for name, g, r in zip(("dQ", "dK", "dV"), grads, g_ref):
+            check_grad(w.dtype, g[:, h:h + 1].cpu(), r, f"head {h} {name}")
+
+
+def test_varlen_mix_full_size(dev):
+    """The packed length mix (16 sequences, 256..4096 tokens, 16 heads), two heads
+    against the oracle."""
+    w = VARLEN_WORKLOADS["varlen_mix"]
+    x = make_varlen_inputs(w)
+    say(f"[varlen_mix] T={x['q'].shape[1]} max={x['max_len']}")
+    cu = x["cu"].to(dev)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd_ex(q, k, v, w.scale, w.causal, cu_seqlens=cu, max_seqlen=x["max_len"])
+    grads = fa.bwd_ex(q, k, v, o, do, lse, w.scale, w.causal, cu_seqlens=cu, max_seqlen=x["max_len"])
+    torch.cuda.synchronize()
+    cuh = x["cu"].numpy()
+    for h in (0, w.H - 1):
+        sl = lambda t: to_f64(t[h:h + 1])
+        O_ref, lse_ref = varlen_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), cuh, w.scale, w.causal)
+        check_fwd(w.dtype, o[h:h + 1].cpu(), lse[h:h + 1].cpu(), O_ref, lse_ref, f"head {h}")
+        g_ref = varlen_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["do"]), cuh, w.scale, w.causal)
+        for name, g, r in zip(("dQ", "dK", "dV"), grads, g_ref):
+            check_grad(w.dtype, g[h:h + 1].cpu(), r, f"head {h} {name}")
+
+
+def test_ex_invalid_args(dev):
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16, device=dev)
+    for causal, window in ((False, 5), (True, -1)):
+        with pytest.raises(fa.FaError) as e:
+            fa.fwd_ex(q, q, q, None, causal, window)
+        assert e.value.status == fa.FA_ERR_INVALID_ARG
+    qp = torch.zeros((1, 64, 64), dtype=torch.bfloat16, device=dev)
+    cu = torch.tensor([0, 0, 64], dtype=torch.int32, device=dev)
+    raw = torch.zeros(16, dtype=torch.uint8, device=dev)
+    r = fa.lib().fa_fwd_ex(qp.data_ptr(), qp.data_ptr(), qp.data_ptr(), qp.data_ptr(), raw.data_ptr(),
+                           cu.data_ptr() + 2, 2, 1, 64, 64, 64, 0.125, 1, 0, fa.FA_DTYPE_BF16, 0)
+    assert r == fa.FA_ERR_INVALID_ARG  # misaligned cu_seqlens
