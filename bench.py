@@ -155,6 +155,130 @@ def decode_measure(dev, steps: int, warmup: int, cpu: bool):
     return rec
 
 
+def _timed(calls, steps: int, warmup: int):
+    """Average HIP-event time (ms) of each callable, run in sequence per step."""
+    import torch
+
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for e in evs:
+        for i, c in enumerate(calls):
+            e[i].record()
+            c()
+        e[len(calls)].record()
+    torch.cuda.synchronize()
+    return [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(len(calls))]
+
+
+def ex_measure(dev, steps: int, warmup: int, cpu: bool):
+    """Sliding window (window_long) and variable-length batch (varlen_mix): fwd and bwd
+    time, credited TFLOP/s over the visible pairs, and the same data without the
+    feature (plain causal; zero-padded dense batch) timed beside it."""
+    import numpy as np
+    import torch
+
+    from exact_io_aware_14_amd import fa
+    from exact_io_aware_14_amd.accounting import varlen_pairs, window_pairs
+    from exact_io_aware_14_amd.inputs import (VARLEN_WORKLOADS, WINDOW_WORKLOADS, make_inputs,
+                                              make_varlen_inputs, to_f64)
+
+    out = {}
+    # --- sliding window ----------------------------------------------------------
+    w, W = WINDOW_WORKLOADS["window_long"]
+    x = make_inputs(w)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd_ex(q, k, v, w.scale, True, W)
+    ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    t_f, t_b = _timed([lambda: fa.fwd_ex(q, k, v, w.scale, True, W, out=o, lse=lse),
+                       lambda: fa.bwd_ex(q, k, v, o, do, lse, w.scale, True, W, workspace=ws, grads=grads)],
+                      steps, warmup)
+    o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+    c_f, c_b = _timed([lambda: fa.fwd(q, k, v, w.scale, True, out=o2, lse=lse2),
+                       lambda: fa.bwd(q, k, v, o2, do, lse2, w.scale, True, workspace=ws, grads=grads)],
+                      steps, warmup)
+    ff = 4.0 * w.d * w.B * w.H * window_pairs(w.N, W)
+    rec = {"workload": {"name": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "window": W,
+                        "dtype": w.dtype},
+           "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+           "fwd_tflops": round(ff / t_f / 1e9, 1), "bwd_tflops": round(2.5 * ff / t_b / 1e9, 1),
+           "causal_without_window_ms": {"fwd": round(c_f, 4), "bwd": round(c_b, 4)},
+           "speedup_vs_causal": round((c_f + c_b) / (t_f + t_b), 3),
+           "visible_pair_ratio": round(window_pairs(w.N, 0) / window_pairs(w.N, W), 3),
+           "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(ff / t_f / 1e9, 1),
+                        "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ff / t_f / 1e9 / PEAK_TFLOPS, 4),
+                        "traffic": None}}
+    if cpu:
+        from oracle import attention_bwd, attention_fwd
+        from oracle.varlen import window_mask
+
+        sl = lambda t: to_f64(t[:, :1])
+        Q, K, V, dO = (sl(x[n]) for n in ("q", "k", "v", "do"))
+        t1 = time.perf_counter()
+        m = window_mask(w.N, W)
+        O_ref, _ = attention_fwd(Q, K, V, w.scale, True, mask=m)
+        attention_bwd(Q, K, V, dO, w.scale, True, mask=m)
+        t = time.perf_counter() - t1
+        rec["cpu_baseline"] = {"value": round(3.5 * ff / (w.B * w.H) / t / 1e12, 5), "unit": "TFLOP/s",
+                               "kind": "oracle", "sample": f"fwd+bwd of head (0,0), {t:.1f} s"}
+        rec["parity_sample"] = {"O_maxabs_head0": float(np.abs(o[:, :1].float().cpu().numpy() - O_ref).max())}
+    out["window_long"] = rec
+
+    # --- variable-length batch ---------------------------------------------------
+    vw = VARLEN_WORKLOADS["varlen_mix"]
+    xv = make_varlen_inputs(vw)
+    cu, nmax = xv["cu"].to(dev), xv["max_len"]
+    lens = np.diff(xv["cu"].numpy())
+    q, k, v, do = (xv[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd_ex(q, k, v, vw.scale, vw.causal, cu_seqlens=cu, max_seqlen=nmax)
+    ws = torch.empty(fa.workspace_bytes(len(lens), vw.H, nmax, vw.d, q.dtype), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    t_f, t_b = _timed([lambda: fa.fwd_ex(q, k, v, vw.scale, vw.causal, cu_seqlens=cu, max_seqlen=nmax,
+                                         out=o, lse=lse),
+                       lambda: fa.bwd_ex(q, k, v, o, do, lse, vw.scale, vw.causal, cu_seqlens=cu,
+                                         max_seqlen=nmax, workspace=ws, grads=grads)], steps, warmup)
+    # the same sequences zero-padded to the longest one, as a dense [B, H, max, d] batch
+    B = len(lens)
+    pad = lambda t: torch.zeros((B, vw.H, nmax, vw.d), dtype=t.dtype, device=dev)
+    qp, kp, vp, dop = pad(q), pad(k), pad(v), pad(do)
+    cuh = xv["cu"].numpy()
+    for b in range(B):
+        for src, dst in ((q, qp), (k, kp), (v, vp), (do, dop)):
+            dst[b, :, :lens[b]] = src[:, cuh[b]:cuh[b + 1]]
+    op, lsp = fa.fwd(qp, kp, vp, vw.scale, vw.causal)
+    wsp = torch.empty(fa.workspace_bytes(B, vw.H, nmax, vw.d, q.dtype), dtype=torch.uint8, device=dev)
+    gp = tuple(torch.empty_like(qp) for _ in range(3))
+    p_f, p_b = _timed([lambda: fa.fwd(qp, kp, vp, vw.scale, vw.causal, out=op, lse=lsp),
+                       lambda: fa.bwd(qp, kp, vp, op, dop, lsp, vw.scale, vw.causal, workspace=wsp, grads=gp)],
+                      steps, warmup)
+    ff = 4.0 * vw.d * vw.H * varlen_pairs(lens, vw.causal)
+    rec = {"workload": {"name": vw.name, "sequences": B, "lengths": [int(n) for n in lens],
+                        "total": int(lens.sum()), "max_len": nmax, "H": vw.H, "d": vw.d,
+                        "causal": vw.causal, "dtype": vw.dtype},
+           "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+           "fwd_tflops": round(ff / t_f / 1e9, 1), "bwd_tflops": round(2.5 * ff / t_b / 1e9, 1),
+           "padded_dense_ms": {"fwd": round(p_f, 4), "bwd": round(p_b, 4)},
+           "speedup_vs_padded": round((p_f + p_b) / (t_f + t_b), 3),
+           "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(ff / t_f / 1e9, 1),
+                        "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ff / t_f / 1e9 / PEAK_TFLOPS, 4),
+                        "traffic": None}}
+    if cpu:
+        from oracle.varlen import varlen_fwd
+
+        sl = lambda t: to_f64(t[:1])
+        t1 = time.perf_counter()
+        O_ref, _ = varlen_fwd(sl(xv["q"]), sl(xv["k"]), sl(xv["v"]), cuh, vw.scale, vw.causal)
+        t = time.perf_counter() - t1
+        rec["cpu_baseline"] = {"value": round(ff / vw.H / t / 1e12, 5), "unit": "TFLOP/s", "kind": "oracle",
+                               "sample": f"forward of head 0, all sequences, {t:.1f} s"}
+        rec["parity_sample"] = {"O_maxabs_head0": float(np.abs(o[:1].float().cpu().numpy() - O_ref).max())}
+    out["varlen_mix"] = rec
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +404,7 @@ def main(argv=None) -> int:
         rec["cpu_baseline"] = None
     if not args.no_next:
         rec["next_rows"] = {"splitkv_decode": decode_measure(dev, args.steps, args.warmup, args.cpu_heads > 0)}
+        rec["next_rows"].update(ex_measure(dev, min(args.steps, 10), min(args.warmup, 3), args.cpu_heads > 0))
     print(json.dumps(rec), flush=True)
     return 0
 
