@@ -171,12 +171,15 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   // K and V only ever feed the matrix cores, which read A/B operands from AGPRs as
   // well; keeping them there leaves the VGPRs for operand prefetch.
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) asm volatile("" : "+a"(kop[kk]), "+a"(vop[kk]));
+  for (int kk = 0; kk < NKK; ++kk) asm volatile("s_nop 3" : "+a"(kop[kk]), "+a"(vop[kk]));
+  // dK^T, dV^T accumulators in AGPRs (written by v_accvgpr_write: 4 wait states
+  // before the first product accumulates into them).
   f32x16_t dk[NDT], dv[NDT];
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) {
     dk[dt] = zero16();
     dv[dt] = zero16();
+    asm volatile("s_nop 3" : "+a"(dk[dt]), "+a"(dv[dt]));
   }
   const float c = scale * kLog2e;
   // query tiles of this sequence (its padded rows hold lse = +inf: P = 0 there) ...
@@ -223,16 +226,32 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
         bg[j][dt] = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
         bq[j][dt] = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
       }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK + 8 * NDT, 0);
+    // lse (base 2) and D of the tile's query rows crow(g, r): four consecutive rows
+    // per 128-bit read of the padded vectors.
+    float lv[16], dvv[16];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float4 l4 = *reinterpret_cast<const float4*>(Lb + 8 * b + 4 * g);
+      const float4 d4 = *reinterpret_cast<const float4*>(Eb + 8 * b + 4 * g);
+      lv[4 * b] = l4.x, lv[4 * b + 1] = l4.y, lv[4 * b + 2] = l4.z, lv[4 * b + 3] = l4.w;
+      dvv[4 * b] = d4.x, dvv[4 * b + 1] = d4.y, dvv[4 * b + 2] = d4.z, dvv[4 * b + 3] = d4.w;
+    }
+    __builtin_amdgcn_sched_barrier(0);
 
-    // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes.
-    f32x16_t s = zero16(), dp = zero16();
+    // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes; the
+    // results land in VGPRs, where the softmax below reads them.
+    f32x16_t s, dp;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq[kk], kop[kk], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[kk], vop[kk], dp, 0, 0, 0);
+      if (kk == 0) {
+        mma_v_first(s, aq[0], kop[0]);
+        mma_v_first(dp, ag[0], vop[0]);
+      } else {
+        mma_v(s, aq[kk], kop[kk]);
+        mma_v(dp, ag[kk], vop[kk]);
+      }
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NKK, 0);
+    mfma_v_ready(s, dp);
 
     // Keys past the end and, on tiles crossing the diagonal, keys above it: S = -inf,
     // so P = 2^-inf = 0 and dS = 0.  Only those tiles pay for the per-element test.
@@ -245,30 +264,22 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       }
     }
 
-    // The previous tile's dV/dK products, overlapping this tile's softmax below.
+    // The previous tile's dV/dK products (accumulating in AGPRs), each followed by
+    // one element of this tile's P = 2^(s*c - lse2) and dS = P (dP - D) on the
+    // vector ALUs; sched_barrier keeps that interleave.
+    constexpr int NSTEP = 2 * NDT, EPS = 16 / NSTEP;  // product pairs; elements per pair
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < NSTEP; ++i) {
+      const int j = i / NDT, dt = i % NDT;
+      mma_a(dv[dt], pa[j], bg[j][dt]);
+      mma_a(dk[dt], da[j], bq[j][dt]);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[j], bg[j][dt], dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[j], bq[j][dt], dk[dt], 0, 0, 0);
-      }
-
-    // This tile's P = 2^(s*c - lse2) and dS = P (dP - D), on the vector ALUs while
-    // the products above run.  Query rows crow(g, r): four consecutive rows per
-    // 128-bit read of the padded lse / D vectors.
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float4 l4 = *reinterpret_cast<const float4*>(Lb + 8 * b + 4 * g);
-      const float4 d4 = *reinterpret_cast<const float4*>(Eb + 8 * b + 4 * g);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int r = 4 * b + t;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[t]));
+      for (int r = i * EPS; r < i * EPS + EPS; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[r]));
         s[r] = p;
-        dp[r] = p * (dp[r] - dvv[t]);
+        dp[r] = p * (dp[r] - dvv[r]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -277,12 +288,7 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
         pa[j][t] = (__bf16)s[8 * j + t];
         da[j][t] = (__bf16)dp[8 * j + t];
       }
-    // Order for this part: each dV/dK product followed by a slice of the softmax.
-#pragma unroll
-    for (int i = 0; i < 4 * NDT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);
-    }
+    valu_ready(pa[0], pa[1], da[0], da[1]);  // read by the next step's products
   };
 
   // The first step reads its "previous" dV/dK operands from Q2/G2, which nothing has
@@ -312,11 +318,15 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       for (int dt = 0; dt < NDT; ++dt) {
         const bf16x8_t bg = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
         const bf16x8_t bq = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[j], bg, dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[j], bq, dk[dt], 0, 0, 0);
+        mma_a(dv[dt], pa[j], bg);
+        mma_a(dk[dt], da[j], bq);
       }
   }
 
+  // MFMA results in AGPRs: 16 wait states before v_accvgpr_read may take them.
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dk[0]), "+a"(dv[0]));
+#pragma unroll
+  for (int dt = 1; dt < NDT; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
   // dK (scaled) and dV: lane = dim column, register = key row.
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt)

@@ -138,6 +138,41 @@ __device__ __forceinline__ void seq_rows(const SeqMap& m, int bh, int Nmax, int&
   len = min(c1 - c0, Nmax);
 }
 
+// --- Matrix products with fixed register files ----------------------------------
+// The compiler picks one form for every MFMA builtin of a kernel: when a kernel
+// may use more than 256 registers, all accumulators go to AGPRs, and scores that
+// the vector ALUs must read are then copied out on every tile.  The wrappers below
+// state each operand's file instead (S in VGPRs next to the softmax, O in AGPRs,
+// Q^T in AGPRs).  The compiler does not model the hazards of an instruction inside
+// inline asm, so the code that mixes these with vector code keeps the wait states
+// gfx950 requires with the mfma_*_ready helpers:
+//   * a vector-ALU read or write of an MFMA result: 16 wait states after the MFMA
+//     (the compiler itself inserts 12-13 for this 8-pass instruction);
+//   * an MFMA reading a register just written by the vector ALU or by
+//     v_accvgpr_write: 4 (the documented need is 2).
+// Dependent MFMAs (one accumulating into the result of an earlier one) need no
+// wait states of their own.
+// acc = a * b (first product of a chain); acc in VGPRs, b in AGPRs.
+__device__ __forceinline__ void mma_v_first(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
+// acc += a * b; acc in VGPRs, b in AGPRs.
+__device__ __forceinline__ void mma_v(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// acc += a * b; acc in AGPRs, a and b in VGPRs.
+__device__ __forceinline__ void mma_a(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// MFMA results in VGPRs may now be touched by vector code.
+__device__ __forceinline__ void mfma_v_ready(f32x16_t& x, f32x16_t& y) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+}
+// Vector-written MFMA operands in VGPRs may now be read by an MFMA.
+__device__ __forceinline__ void valu_ready(bf16x8_t& a, bf16x8_t& b, bf16x8_t& c, bf16x8_t& d) {
+  asm volatile("s_nop 3" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 // Start value of the running max: finite, so that exp2((m_old - m_new) * c) and
 // s * c - m * c never form -inf - (-inf) while a row has seen no visible key.
