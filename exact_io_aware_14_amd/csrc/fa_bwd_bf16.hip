@@ -53,11 +53,6 @@ __device__ __forceinline__ int bswz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-__device__ __forceinline__ void dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
-}
-
 __device__ __forceinline__ bf16x8_t tr_pair(const __bf16* lo, const __bf16* hi) {
   const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)lo);
   const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)hi);
@@ -123,15 +118,18 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     q_col[i] = (p ^ bswz<D>(r)) * 8;
   }
   auto issue_q = [&](int qt, __bf16* Qd, __bf16* Gd, float* Ld, float* Ed) {
-    const int qb0 = qt * C::BQ;
+    const int qb0 = qt * C::BQ;  // < N: every streamed tile holds a valid row
+    const __bf16* qs = Q + head + (size_t)qb0 * D;
+    const __bf16* gs = dO + head + (size_t)qb0 * D;
 #pragma unroll
     for (int i = 0; i < C::QLOADS; ++i) {
-      const int row = min(qb0 + q_row[i], N - 1);  // padding rows: any valid row (P = 0 there)
-      dma16(Q + head + (size_t)row * D + q_col[i], Qd + (w * C::QLOADS + i) * 512);
-      dma16(dO + head + (size_t)row * D + q_col[i], Gd + (w * C::QLOADS + i) * 512);
+      // padding rows past N read the last row (P = 0 there)
+      const unsigned off = (unsigned)(min(q_row[i], N - 1 - qb0) * D + q_col[i]) * 2u;
+      dma16(qs, off, Qd + (w * C::QLOADS + i) * 512);
+      dma16(gs, off, Gd + (w * C::QLOADS + i) * 512);
     }
-    if (w == 0 && lane < C::BQ / 4) dma16(L2 + hpad + qb0 + 4 * lane, Ld);
-    if (w == 1 && lane < C::BQ / 4) dma16(Dvec + hpad + qb0 + 4 * lane, Ed);
+    if (w == 0 && lane < C::BQ / 4) dma16(L2 + hpad + qb0, 16u * lane, Ld);
+    if (w == 1 && lane < C::BQ / 4) dma16(Dvec + hpad + qb0, 16u * lane, Ed);
   };
   // --- per-lane LDS read offsets -------------------------------------------------
   // Natural A-operand read of row l32, logical chunk 2*kk + g.

@@ -42,11 +42,6 @@ __device__ __forceinline__ int dq_swz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-__device__ __forceinline__ void dq_dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
-}
-
 template <int D, bool GEN>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
@@ -90,12 +85,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     src_col[i] = (p ^ dq_swz<D>(r)) * 8;
   }
   auto issue_tile = [&](int kt, __bf16* Kd, __bf16* Vd) {
-    const int kbase = kt * C::BC;
+    const int kbase = kt * C::BC;  // < N for every tile issued
+    const __bf16* ks = K + head + (size_t)kbase * D;
+    const __bf16* vs = V + head + (size_t)kbase * D;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int row = min(kbase + src_row[i], N - 1);  // keys past the end are masked
-      dq_dma16(K + head + (size_t)row * D + src_col[i], Kd + (w * C::LOADS + i) * 512);
-      dq_dma16(V + head + (size_t)row * D + src_col[i], Vd + (w * C::LOADS + i) * 512);
+      // keys past the end read the last row (masked later)
+      const unsigned off = (unsigned)(min(src_row[i], N - 1 - kbase) * D + src_col[i]) * 2u;
+      dma16(ks, off, Kd + (w * C::LOADS + i) * 512);
+      dma16(vs, off, Vd + (w * C::LOADS + i) * 512);
     }
   };
   // natural A-operand reads: row ks*32 + l32, logical chunk 2*kk + g

@@ -104,6 +104,25 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
 
+// One direct global -> LDS load of 16 bytes per lane: lane l's bytes come from
+// base + voff (base wave-uniform, voff in bytes) and land at lds_wave + 16*l, so the
+// loaded data never passes through VGPRs.  Issued as inline assembly: with the
+// compiler builtin for this load, the compiler counts it as an LDS access of
+// unknown order and then uses full drains (lgkmcnt(0)) for every LDS wait in the
+// kernel, so LDS reads can no longer run ahead of the matrix products that consume
+// them.  The compiler therefore does not track these loads: every caller waits for
+// them itself (s_waitcnt vmcnt(0), then a barrier) before the tile is read.
+__device__ __forceinline__ void dma16(const void* base, unsigned voff, const void* lds_wave) {
+  const unsigned long long t = (unsigned long long)base;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)t);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(t >> 32));
+  const unsigned long long sbase = ((unsigned long long)hi << 32) | lo;
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(
+      (unsigned)(unsigned long long)(const __attribute__((address_space(3))) void*)lds_wave);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+               : "memory", "m0");
+}
+
 // Block id -> logical work id.  Consecutive workgroup ids are spread round robin
 // over the 8 XCDs (each with its own L2); the remap hands each XCD a contiguous
 // range of logical ids, so the tiles of one (batch, head) share that XCD's L2.

@@ -40,6 +40,8 @@ struct FwdFast {
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;       // query rows per workgroup
   static constexpr int BC = 64;            // keys per K/V tile
+  static constexpr int NKS = BC / 32;      // 32-key halves of a tile
+  static constexpr int OCC = 2;            // waves per SIMD the registers are sized for
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int TILE = BC * D;      // elements per K (or V) tile
   static constexpr int LOADS = BC * CPR / 64 / NW;  // direct loads per wave per tile
@@ -58,13 +60,8 @@ __device__ __forceinline__ int vswz(int r) {
   return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
 }
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
-                                   (void __attribute__((address_space(3)))*)lds_wave_base, 16, 0, 0);
-}
-
 template <int D, bool GEN>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int Nmax, float scale, int causal, int nqb,
     SeqMap sm_arg, int window_arg) {
@@ -115,16 +112,32 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     v_src_row[i] = r;
     v_src_col[i] = (p ^ vswz<D>(r)) * 8;
   }
+  // The same pieces as offsets from a tile's first row: a load is then a wave-uniform
+  // tile base plus a fixed per-lane offset, with no per-tile address arithmetic.
+  unsigned k_off[C::LOADS], v_off[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    k_off[i] = k_src_row[i] * D + k_src_col[i];
+    v_off[i] = v_src_row[i] * D + v_src_col[i];
+  }
   auto issue_tile = [&](int kt, __bf16* Kd, __bf16* Vd) {
     const int kbase = kt * C::BC;
+    const __bf16* ks = Kh + (size_t)kbase * D;
+    const __bf16* vs = Vh + (size_t)kbase * D;
+    if (kbase + C::BC <= N) {
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const int kr = min(kbase + k_src_row[i], N - 1);  // rows past the end: any valid row, masked later
-      const int vr = min(kbase + v_src_row[i], N - 1);
-      __bf16* kdst = Kd + (w * C::LOADS + i) * 64 * 8;
-      __bf16* vdst = Vd + (w * C::LOADS + i) * 64 * 8;
-      lds_dma16(Kh + (size_t)kr * D + k_src_col[i], kdst);
-      lds_dma16(Vh + (size_t)vr * D + v_src_col[i], vdst);
+      for (int i = 0; i < C::LOADS; ++i) {
+        dma16(ks, k_off[i] * 2u, Kd + (w * C::LOADS + i) * 64 * 8);
+        dma16(vs, v_off[i] * 2u, Vd + (w * C::LOADS + i) * 64 * 8);
+      }
+    } else {  // the tile runs past the end: rows past it read the last row (masked later)
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const int kr = min(k_src_row[i], N - 1 - kbase);
+        const int vr = min(v_src_row[i], N - 1 - kbase);
+        dma16(ks, (unsigned)(kr * D + k_src_col[i]) * 2u, Kd + (w * C::LOADS + i) * 64 * 8);
+        dma16(vs, (unsigned)(vr * D + v_src_col[i]) * 2u, Vd + (w * C::LOADS + i) * 64 * 8);
+      }
     }
   };
   // K operand read (A of S^T = K Q^T): row ks*32 + l32, chunk 2*kk + g.
@@ -172,23 +185,38 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     if (causal && k0 > qw + 31) return;  // tile wholly above this wave's rows
     if (window > 0 && k0 + C::BC - 1 <= qw - window) return;  // wholly below their band
     // S^T = K Q^T
-    f32x16_t s[2];
-    s[0] = zero16();
-    s[1] = zero16();
+    constexpr int NKS = C::NKS;
+    // K operand reads run AHEAD d-steps in front of the products that use them, so
+    // the LDS round trips overlap each other and the products instead of alternating
+    // with them (at most 15 LDS reads may be outstanding for a counted wait).
+    constexpr int AHEAD = NKK < 4 ? NKK : 4;
+    f32x16_t s[NKS];
+    bf16x8_t ka[NKK][NKS];
+    auto read_k = [&](int kk) {
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+      for (int ks = 0; ks < NKS; ++ks)
+        ka[kk][ks] = *reinterpret_cast<const bf16x8_t*>(
             Kb + k_rd + (ks * 2 * CPR * 16 + kk * 2 * 16) * 8);
-        s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[kk], s[ks], 0, 0, 0);
-      }
+    };
+#pragma unroll
+    for (int kk = 0; kk < AHEAD; ++kk) read_k(kk);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) s[ks] = zero16();
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + AHEAD < NKK) read_k(kk + AHEAD);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][ks], qop[kk], s[ks], 0, 0, 0);
+    }
 
     const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw) ||
                            (window > 0 && k0 <= qw + 31 - window);
     if (need_mask) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + ks * 32 + crow(g, r);
@@ -202,8 +230,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    for (int ks = 1; ks < NKS; ++ks)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
+    {  // the other half of the wave holds the other keys of the same query columns
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
     const bool move = mx > mref + grow;
     if (__builtin_amdgcn_ballot_w64(move)) {  // wave-uniform: rare after the first tile
       const float mnew = move ? mx : mref;
@@ -216,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     }
     const float mc = mref * c;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
@@ -226,7 +259,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
     // O^T += V^T P^T
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8_t pb;
