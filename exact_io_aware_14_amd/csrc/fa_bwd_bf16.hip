@@ -80,20 +80,27 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   constexpr int NDT = C::NDT;
   constexpr int CPR = C::CPR;
 
+  // Four sets of Q, dO, lse and D tile buffers, each named statically in the (four
+  // times unrolled) step loop: tile t+2 lands while tiles t-1, t and t+1 are read.
   __shared__ __attribute__((aligned(1024))) __bf16 Q0[C::QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 Q1[C::QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 Q2[C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 Q3[C::QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 G0[C::QTILE];  // dO
   __shared__ __attribute__((aligned(1024))) __bf16 G1[C::QTILE];
   __shared__ __attribute__((aligned(1024))) __bf16 G2[C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 G3[C::QTILE];
   __shared__ __attribute__((aligned(16))) float L0[C::BQ];
   __shared__ __attribute__((aligned(16))) float L1[C::BQ];
   __shared__ __attribute__((aligned(16))) float L2s[C::BQ];
+  __shared__ __attribute__((aligned(16))) float L3[C::BQ];
   __shared__ __attribute__((aligned(16))) float E0[C::BQ];  // D values
   __shared__ __attribute__((aligned(16))) float E1[C::BQ];
   __shared__ __attribute__((aligned(16))) float E2[C::BQ];
+  __shared__ __attribute__((aligned(16))) float E3[C::BQ];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / nkb;
@@ -196,26 +203,47 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       pa[j][t] = (__bf16)0.0f;
       da[j][t] = (__bf16)0.0f;
     }
+  // Q and dO rows of the next tile (A operands of its S and dP), read one step ahead
+  // straight into AGPRs: the S and dP products of a step then start right after its
+  // barrier, and these reads run under the previous step's dV/dK products.
+  bf16x8_t aq[NKK], ag[NKK];
+  auto prefetch_rows = [&](const __bf16* Qb, const __bf16* Gb, int kk) {
+    lds_read_a(aq[kk], Qb + nat[kk]);
+    lds_read_a(ag[kk], Gb + nat[kk]);
+  };
 
-  // One pipelined step, a single basic block: tile qt's S, dP, P, dS and tile qt-1's
-  // dV, dK.  Tiles where every key of this wave lies above the diagonal come out
-  // fully masked (P = dS = 0), so no branch is needed for them.
-  auto tile = [&](int qt, const __bf16* Qb, const __bf16* Gb, const float* Lb, const float* Eb,
-                  const __bf16* Qp, const __bf16* Gp, __bf16* Qn, __bf16* Gn, float* Ln, float* En) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile qt landed
-    __syncthreads();                     // ... everyone's; tile qt-2's buffers are free
-    if (qt + 1 < nqt) issue_q(qt + 1, Qn, Gn, Ln, En);
+  // Step qt (tile t in buffer set (t - qt0) % 4; p = tile qt-1, c = tile qt, n = tile
+  // qt+1, i = tile qt+2):
+  //   wait until tile qt+1 has landed everywhere and this wave's reads of tile qt's
+  //   rows are back; start tile qt+2 (its set last held tile qt-2, whose final reads
+  //   were in step qt-1);
+  //   S, dP of tile qt from the prefetched rows; read tile qt-1's transposed dO and Q
+  //   (B operands of its dV, dK) and tile qt's lse and D while they run;
+  //   tile qt-1's dV/dK products, each followed by a slice of tile qt's softmax and
+  //   two reads of tile qt+1's rows (past the last tile: stale, never used).
+  auto step = [&](int qt, const __bf16* Qp, const __bf16* Gp, const float* Lc, const float* Ec,
+                  const __bf16* Qn, const __bf16* Gn, __bf16* Qi, __bf16* Gi, float* Li, float* Ei) {
+    __builtin_amdgcn_sched_barrier(0);  // no code motion across steps
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (qt + 2 < nqt) issue_q(qt + 2, Qi, Gi, Li, Ei);
     const int qb0 = qt * C::BQ;
 
-    // Operand reads for the whole step, issued before any product that uses them:
-    // Q and dO rows (A operands of S and dP) and, from the previous tile's buffers,
-    // dO and Q transposed (B operands of dV and dK).  One LDS latency per step.
-    bf16x8_t aq[NKK], ag[NKK];
+    // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes; the
+    // results land in VGPRs, where the softmax below reads them.
+    f32x16_t s, dp;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      aq[kk] = *reinterpret_cast<const bf16x8_t*>(Qb + nat[kk]);
-      ag[kk] = *reinterpret_cast<const bf16x8_t*>(Gb + nat[kk]);
+      if (kk == 0) {
+        mma_v_first_aa(s, aq[0], kop[0]);
+        mma_v_first_aa(dp, ag[0], vop[0]);
+      } else {
+        mma_v_aa(s, aq[kk], kop[kk]);
+        mma_v_aa(dp, ag[kk], vop[kk]);
+      }
     }
+    // Operand reads of this step, issued while the products above run.
     bf16x8_t bg[2][NDT], bq[2][NDT];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -229,25 +257,10 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     float lv[16], dvv[16];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float4 l4 = *reinterpret_cast<const float4*>(Lb + 8 * b + 4 * g);
-      const float4 d4 = *reinterpret_cast<const float4*>(Eb + 8 * b + 4 * g);
+      const float4 l4 = *reinterpret_cast<const float4*>(Lc + 8 * b + 4 * g);
+      const float4 d4 = *reinterpret_cast<const float4*>(Ec + 8 * b + 4 * g);
       lv[4 * b] = l4.x, lv[4 * b + 1] = l4.y, lv[4 * b + 2] = l4.z, lv[4 * b + 3] = l4.w;
       dvv[4 * b] = d4.x, dvv[4 * b + 1] = d4.y, dvv[4 * b + 2] = d4.z, dvv[4 * b + 3] = d4.w;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes; the
-    // results land in VGPRs, where the softmax below reads them.
-    f32x16_t s, dp;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      if (kk == 0) {
-        mma_v_first(s, aq[0], kop[0]);
-        mma_v_first(dp, ag[0], vop[0]);
-      } else {
-        mma_v(s, aq[kk], kop[kk]);
-        mma_v(dp, ag[kk], vop[kk]);
-      }
     }
     mfma_v_ready(s, dp);
 
@@ -263,14 +276,17 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     }
 
     // The previous tile's dV/dK products (accumulating in AGPRs), each followed by
-    // one element of this tile's P = 2^(s*c - lse2) and dS = P (dP - D) on the
-    // vector ALUs; sched_barrier keeps that interleave.
+    // elements of this tile's P = 2^(s*c - lse2) and dS = P (dP - D) on the vector
+    // ALUs and by reads of the next tile's rows; sched_barrier keeps that interleave.
     constexpr int NSTEP = 2 * NDT, EPS = 16 / NSTEP;  // product pairs; elements per pair
+    constexpr int RPS = (NKK + NSTEP - 1) / NSTEP;    // row-operand steps read per pair
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
       const int j = i / NDT, dt = i % NDT;
       mma_a(dv[dt], pa[j], bg[j][dt]);
       mma_a(dk[dt], da[j], bq[j][dt]);
+#pragma unroll
+      for (int kk = i * RPS; kk < i * RPS + RPS && kk < NKK; ++kk) prefetch_rows(Qn, Gn, kk);
 #pragma unroll
       for (int r = i * EPS; r < i * EPS + EPS; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[r]));
@@ -289,27 +305,37 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     valu_ready(pa[0], pa[1], da[0], da[1]);  // read by the next step's products
   };
 
-  // The first step reads its "previous" dV/dK operands from Q2/G2, which nothing has
-  // written yet: zero them, since 0 * (an Inf or NaN bit pattern) would not be 0.
-  // The first step's barrier orders these writes before any later load into them.
+  // Prologue: tiles qt0 and qt0+1 loading, then tile qt0's rows.  The first step reads
+  // its "previous" dV/dK operands from Q3/G3, which nothing has loaded: zero them,
+  // since 0 * (an Inf or NaN bit pattern) would not be 0.  The prologue's barrier
+  // orders these writes before those reads, and the first load into Q3/G3 comes
+  // after the second step's barrier.
   for (int i = tid; i < C::QTILE / 8; i += C::NT) {
-    reinterpret_cast<v16b*>(Q2)[i] = v16b{0, 0, 0, 0};
-    reinterpret_cast<v16b*>(G2)[i] = v16b{0, 0, 0, 0};
+    reinterpret_cast<v16b*>(Q3)[i] = v16b{0, 0, 0, 0};
+    reinterpret_cast<v16b*>(G3)[i] = v16b{0, 0, 0, 0};
   }
   issue_q(qt0, Q0, G0, L0, E0);
+  if (qt0 + 1 < nqt) issue_q(qt0 + 1, Q1, G1, L1, E1);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) prefetch_rows(Q0, G0, kk);
   int qt = qt0;
-  for (; qt + 2 < nqt; qt += 3) {  // whole rotations: no conditional steps in the body
-    tile(qt, Q0, G0, L0, E0, Q2, G2, Q1, G1, L1, E1);
-    tile(qt + 1, Q1, G1, L1, E1, Q0, G0, Q2, G2, L2s, E2);
-    tile(qt + 2, Q2, G2, L2s, E2, Q1, G1, Q0, G0, L0, E0);
+  for (; qt + 3 < nqt; qt += 4) {  // whole rotations: no conditional steps in the body
+    step(qt, Q3, G3, L0, E0, Q1, G1, Q2, G2, L2s, E2);
+    step(qt + 1, Q0, G0, L1, E1, Q2, G2, Q3, G3, L3, E3);
+    step(qt + 2, Q1, G1, L2s, E2, Q3, G3, Q0, G0, L0, E0);
+    step(qt + 3, Q2, G2, L3, E3, Q0, G0, Q1, G1, L1, E1);
   }
-  if (qt < nqt) tile(qt, Q0, G0, L0, E0, Q2, G2, Q1, G1, L1, E1);
-  if (qt + 1 < nqt) tile(qt + 1, Q1, G1, L1, E1, Q0, G0, Q2, G2, L2s, E2);
-  // dV/dK of the last tile (its buffers are still intact: no further loads were issued)
+  if (qt < nqt) step(qt, Q3, G3, L0, E0, Q1, G1, Q2, G2, L2s, E2);
+  if (qt + 1 < nqt) step(qt + 1, Q0, G0, L1, E1, Q2, G2, Q3, G3, L3, E3);
+  if (qt + 2 < nqt) step(qt + 2, Q1, G1, L2s, E2, Q3, G3, Q0, G0, L0, E0);
+  // dV/dK of the last tile (buffer set (nqt - 1 - qt0) % 4, intact: no later loads)
   {
-    const int last = (nqt - 1 - qt0) % 3;
-    const __bf16* Qp = last == 0 ? Q0 : last == 1 ? Q1 : Q2;
-    const __bf16* Gp = last == 0 ? G0 : last == 1 ? G1 : G2;
+    const int last = (nqt - 1 - qt0) % 4;
+    const __bf16* Qp = last == 0 ? Q0 : last == 1 ? Q1 : last == 2 ? Q2 : Q3;
+    const __bf16* Gp = last == 0 ? G0 : last == 1 ? G1 : last == 2 ? G2 : G3;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -320,6 +346,8 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
         mma_a(dk[dt], da[j], bq);
       }
   }
+  // No direct load or prefetch read may still be in flight when the wave ends.
+  __builtin_amdgcn_s_waitcnt(0x0070);
 
   // MFMA results in AGPRs: 16 wait states before v_accvgpr_read may take them.
   asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dk[0]), "+a"(dv[0]));

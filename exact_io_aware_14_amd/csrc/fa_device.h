@@ -183,6 +183,22 @@ __device__ __forceinline__ void mma_v(f32x16_t& acc, const bf16x8_t& a, const bf
 __device__ __forceinline__ void mma_a(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// acc = a * b (first product of a chain); acc in VGPRs, a and b in AGPRs.
+__device__ __forceinline__ void mma_v_first_aa(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "a"(a), "a"(b));
+}
+// acc += a * b; acc in VGPRs, a and b in AGPRs.
+__device__ __forceinline__ void mma_v_aa(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "a"(a), "a"(b));
+}
+// 16 bytes of LDS at p (16-byte aligned) straight into AGPRs.  The compiler does not
+// count this read: the caller waits for it (s_waitcnt lgkmcnt(0)) before any
+// instruction reads dst, and keeps it in order with the products that consume dst
+// by issuing those as inline assembly too.
+__device__ __forceinline__ void lds_read_a(bf16x8_t& dst, const __bf16* p) {
+  const unsigned addr = (unsigned)(unsigned long long)(const __attribute__((address_space(3))) void*)p;
+  asm volatile("ds_read_b128 %0, %1" : "=a"(dst) : "v"(addr) : "memory");
+}
 // MFMA results in VGPRs may now be touched by vector code.
 __device__ __forceinline__ void mfma_v_ready(f32x16_t& x, f32x16_t& y) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));

@@ -81,7 +81,8 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) __bf16 V0[C::TILE];
   __shared__ __attribute__((aligned(1024))) __bf16 V1[C::TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   const int bh = id / nqb;
