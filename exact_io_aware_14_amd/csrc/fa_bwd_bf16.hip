@@ -10,8 +10,8 @@
 // avoids one float atomic per key block per dQ element.
 //
 // Data movement for CDNA4:
-// * Q_i, dO_i and the tile's lse/D values are double buffered in LDS by
-//   global_load_lds_dwordx4 (the next tile lands while this one is computed).
+// * Q_i, dO_i and the tile's lse/D values go global -> LDS by global_load_lds_dwordx4,
+//   in four rotating buffer sets: tile i+2 lands while tiles i-1, i and i+1 are read.
 // * Q and dO live in LDS row-major with the 16-byte chunk index XOR-swizzled by
 //   f(r).  The same f makes both reads conflict-free on 64 banks: the natural
 //   128-bit reads of 16 consecutive rows at one chunk (A operands of S and dP), and
@@ -19,12 +19,13 @@
 //   (B operands of dV = P^T dO and dK = dS^T Q).
 // * S = Q K^T and dP = dO V^T put keys on the lane columns of the accumulators, so
 //   P^T and dS^T feed dV and dK as A operands straight from registers.
-// * One wave per SIMD (dK and dV alone hold 128 fp32 per lane at d = 128), so the
-//   overlap comes from inside the wave: the loop is software pipelined.  Iteration
-//   i issues S and dP of tile i, then the dV/dK products of tile i-1 (whose P and
-//   dS wait in registers as bf16), which keep the matrix cores busy while tile i's
-//   P and dS are computed on the vector ALUs.  Q/dO/lse/D tiles are therefore
-//   triple buffered: tile i-1 is still read while tile i+1 lands.
+// * One wave per SIMD (K, V, dK and dV alone hold 192 registers per lane at
+//   d = 128, all in AGPRs), so the overlap comes from inside the wave: the loop is
+//   software pipelined.  Step i starts the S and dP products of tile i from Q/dO
+//   rows already in AGPRs; while they run it reads tile i-1's dO and Q transposed
+//   and tile i's lse and D; then tile i-1's dV/dK products alternate with slices of
+//   tile i's softmax (P and dS on the vector ALUs, kept as bf16 for the next step)
+//   and with the reads of tile i+1's rows into AGPRs.
 #include "fa_device.h"
 #include "fa_launch.h"
 
