@@ -153,13 +153,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
                            (window > 0 && k0 <= qw + 31 - window);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      // K and V operand reads run AHEAD d-steps in front of the products that use them,
+      // so the LDS round trips overlap each other and the products.
+      constexpr int AHEAD = NKK < 4 ? NKK : 3;
       f32x16_t s = zero16(), dp = zero16();
+      bf16x8_t ak[NKK], av[NKK];
+      auto read_kv = [&](int kk) {
+        ak[kk] = *reinterpret_cast<const bf16x8_t*>(Kb + ks * 32 * D + nat[kk]);
+        av[kk] = *reinterpret_cast<const bf16x8_t*>(Vb + ks * 32 * D + nat[kk]);
+      };
+#pragma unroll
+      for (int kk = 0; kk < AHEAD; ++kk) read_kv(kk);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const bf16x8_t ak = *reinterpret_cast<const bf16x8_t*>(Kb + ks * 32 * D + nat[kk]);
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(Vb + ks * 32 * D + nat[kk]);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak, qop[kk], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, gop[kk], dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + AHEAD < NKK) read_kv(kk + AHEAD);
+        __builtin_amdgcn_sched_barrier(0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], qop[kk], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk], gop[kk], dp, 0, 0, 0);
       }
       if (need_mask) {  // keys past the end or above the diagonal: S = -inf, P = 0
 #pragma unroll
