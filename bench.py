@@ -36,7 +36,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+    taken on the kernel's current sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -45,7 +45,7 @@ def measured_traffic(kernel: str, workload: str):
     from exact_io_aware_14_amd.traffic import source_hash
 
     e = t.get(workload, {}).get(kernel)
-    if not e or e.get("source_hash") != source_hash():
+    if not e or e.get("source_hash") != source_hash(kernel):
         return None
     return e.get("hbm_bytes_per_launch")
 

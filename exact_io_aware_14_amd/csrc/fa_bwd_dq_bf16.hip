@@ -119,8 +119,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     if (myq < N) {
-      qop[kk] = *reinterpret_cast<const bf16x8_t*>(Q + head + (size_t)myq * D + kk * 16 + g * 8);
-      gop[kk] = *reinterpret_cast<const bf16x8_t*>(dO + head + (size_t)myq * D + kk * 16 + g * 8);
+      const int off = (myq - q0) * D + kk * 16 + g * 8;
+      qop[kk] = *reinterpret_cast<const bf16x8_t*>(Q + head + (size_t)q0 * D + off);
+      gop[kk] = *reinterpret_cast<const bf16x8_t*>(dO + head + (size_t)q0 * D + off);
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     for (int ks = 0; ks < 2; ++ks) {
       // K and V operand reads run AHEAD d-steps in front of the products that use them,
       // so the LDS round trips overlap each other and the products.
-      constexpr int AHEAD = NKK < 4 ? NKK : 3;
+      constexpr int AHEAD = NKK < 4 ? NKK : 2;
       f32x16_t s = zero16(), dp = zero16();
       bf16x8_t ak[NKK], av[NKK];
       auto read_kv = [&](int kk) {
@@ -220,7 +221,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
 
   // dQ = scale * acc: lane = query row, registers = dims 8 rb + 4 g + 0..3 of tile dt.
   if (myq < N) {
-    __bf16* row = dQ + head + (size_t)myq * D;
+    // wave-uniform block base plus a 32-bit lane offset (no 64-bit value kept live)
+    __bf16* row = dQ + head + (size_t)q0 * D + (myq - q0) * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll

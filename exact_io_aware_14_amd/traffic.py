@@ -73,10 +73,24 @@ def _code_only(text: str) -> str:
     return " ".join(text.split())
 
 
-def source_hash() -> str:
-    """Hash of the kernel sources (comments stripped) the counters belong to."""
+# Source files each kernel's code comes from (besides the shared device headers).
+KERNEL_SOURCES = {
+    "fwd_kernel": ["fa_fwd_bf16.hip"],
+    "bwd_main_kernel": ["fa_bwd_bf16.hip"],
+    "bwd_dq_kernel": ["fa_bwd_dq_bf16.hip"],
+    "bwd_pre_kernel": ["fa_bwd.hip"],
+    "splitkv_partial_kernel": ["fa_decode.hip"],
+    "splitkv_merge_kernel": ["fa_decode.hip"],
+}
+SHARED_SOURCES = ["fa_device.h", "fa_launch.h"]
+
+
+def source_hash(kernel: str | None = None) -> str:
+    """Hash of the sources (comments stripped) a kernel is compiled from: its own file
+    and the shared device headers; with no kernel named, of every source."""
+    names = sorted(os.listdir(CSRC)) if kernel is None else KERNEL_SOURCES[kernel] + SHARED_SOURCES
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in names:
         with open(os.path.join(CSRC, name), encoding="utf-8") as f:
             h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
@@ -130,7 +144,7 @@ def summarize(dirpath: str, workload: str) -> dict:
                 continue
             wl, label = c
             kern = out.setdefault(wl or workload, {})
-            kern.setdefault(label, {"source_hash": res["source_hash"]})
+            kern.setdefault(label, {"source_hash": source_hash(label)})
             kern[label][key] = sum(vals) / len(vals) * 1024.0 * scale
     for wl, kern in out.items():
         if wl == "calibration":
