@@ -136,8 +136,12 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       dma16(qs, off, Qd + (w * C::QLOADS + i) * 512);
       dma16(gs, off, Gd + (w * C::QLOADS + i) * 512);
     }
-    if (w == 0 && lane < C::BQ / 4) dma16(L2 + hpad + qb0, 16u * lane, Ld);
-    if (w == 1 && lane < C::BQ / 4) dma16(Dvec + hpad + qb0, 16u * lane, Ed);
+    if (w < 2) {  // lse on wave 0, D on wave 1: 16 bytes per lane of lanes 0..BQ/4-1
+      // the lane index read afresh, so that it need not stay live across the loop
+      unsigned ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      if (ln < C::BQ / 4) dma16((w == 0 ? L2 : Dvec) + hpad + qb0, 16u * ln, w == 0 ? Ld : Ed);
+    }
   };
   // --- per-lane LDS read offsets -------------------------------------------------
   // Natural A-operand read of row l32, logical chunk 2*kk + g.
@@ -163,8 +167,9 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     if (mykey < N) {
-      kop[kk] = *reinterpret_cast<const bf16x8_t*>(K + head + (size_t)mykey * D + kk * 16 + g * 8);
-      vop[kk] = *reinterpret_cast<const bf16x8_t*>(V + head + (size_t)mykey * D + kk * 16 + g * 8);
+      const int off = (mykey - k0) * D + kk * 16 + g * 8;  // from the block's first key
+      kop[kk] = *reinterpret_cast<const bf16x8_t*>(K + head + (size_t)k0 * D + off);
+      vop[kk] = *reinterpret_cast<const bf16x8_t*>(V + head + (size_t)k0 * D + off);
     } else {
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     for (int r = 0; r < 16; ++r) {
       const int key = kw + crow(g, r);
       if (key < N) {
-        const size_t off = head + (size_t)key * D + dt * 32 + l32;
+        const size_t off = head + (size_t)k0 * D + ((key - k0) * D + dt * 32 + l32);
         dK[off] = (__bf16)(dk[dt][r] * scale);
         dV[off] = (__bf16)dv[dt][r];
       }
