@@ -237,8 +237,30 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     const int qb0 = qt * C::BQ;
 
     // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes; the
-    // results land in VGPRs, where the softmax below reads them.
+    // results land in VGPRs, where the softmax below reads them.  Between the
+    // products go the step's other operand reads: tile qt-1's dO and Q transposed
+    // (B operands of its dV/dK) and tile qt's lse and D, so those LDS round trips
+    // start at once and run under the products instead of after them.
     f32x16_t s, dp;
+    bf16x8_t bg[2][NDT], bq[2][NDT];
+    float lv[16], dvv[16];
+    constexpr int NTR = 4 * NDT;        // transposed 16-byte operands to read
+    constexpr int TPK = NTR / NKK;      // ... per d-step of the products
+    constexpr int LPK = 8 / NKK;        // lse/D 128-bit reads per d-step
+    static_assert(NTR % NKK == 0 && 8 % NKK == 0, "reads must split over the d-steps");
+    auto read_tr = [&](int t) {  // t = (j * NDT + dt) * 2 + (0: dO, 1: Q)
+      const int j = t / (2 * NDT), dt = (t / 2) % NDT;
+      const __bf16* b = (t & 1) ? Qp : Gp;
+      const bf16x8_t v = tr_pair(b + j * 16 * D + trq[0][dt], b + j * 16 * D + trq[1][dt]);
+      if (t & 1) bq[j][dt] = v;
+      else bg[j][dt] = v;
+    };
+    auto read_le = [&](int t) {  // t < 4: lse rows 8t + 4g + 0..3; else D rows
+      const int b = t & 3;
+      const float4 x = *reinterpret_cast<const float4*>((t < 4 ? Lc : Ec) + 8 * b + 4 * g);
+      float* dst = t < 4 ? lv : dvv;
+      dst[4 * b] = x.x, dst[4 * b + 1] = x.y, dst[4 * b + 2] = x.z, dst[4 * b + 3] = x.w;
+    };
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       if (kk == 0) {
@@ -248,25 +270,11 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
         mma_v_aa(s, aq[kk], kop[kk]);
         mma_v_aa(dp, ag[kk], vop[kk]);
       }
-    }
-    // Operand reads of this step, issued while the products above run.
-    bf16x8_t bg[2][NDT], bq[2][NDT];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int t = kk * TPK; t < kk * TPK + TPK; ++t) read_tr(t);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        bg[j][dt] = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
-        bq[j][dt] = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
-      }
-    // lse (base 2) and D of the tile's query rows crow(g, r): four consecutive rows
-    // per 128-bit read of the padded vectors.
-    float lv[16], dvv[16];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float4 l4 = *reinterpret_cast<const float4*>(Lc + 8 * b + 4 * g);
-      const float4 d4 = *reinterpret_cast<const float4*>(Ec + 8 * b + 4 * g);
-      lv[4 * b] = l4.x, lv[4 * b + 1] = l4.y, lv[4 * b + 2] = l4.z, lv[4 * b + 3] = l4.w;
-      dvv[4 * b] = d4.x, dvv[4 * b + 1] = d4.y, dvv[4 * b + 2] = d4.z, dvv[4 * b + 3] = d4.w;
+      for (int t = kk * LPK; t < kk * LPK + LPK; ++t) read_le(t);
+      __builtin_amdgcn_sched_barrier(0);
     }
     mfma_v_ready(s, dp);
 
