@@ -173,6 +173,33 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], qop[kk], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk], gop[kk], dp, 0, 0, 0);
       }
+      // K^T operands of this half's dQ product (transposed reads).  At d = 64 they are
+      // read here, so their LDS round trips run under the softmax below; at d = 128 the
+      // registers for that are not there, and each is read just before its product.
+      auto read_kt = [&](int j, int dt) {
+        const __bf16* kb = Kb + (ks * 32 + j * 16) * D;
+        const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(kb + trk[0][dt]));
+        const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4_t*)(kb + trk[1][dt]));
+        const bf16x4_t x = __builtin_bit_cast(bf16x4_t, lo), y = __builtin_bit_cast(bf16x4_t, hi);
+        bf16x8_t a;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          a[t] = x[t];
+          a[4 + t] = y[t];
+        }
+        return a;
+      };
+      constexpr bool kEarly = D == 64;
+      bf16x8_t kt_op[2][NDT];
+      if constexpr (kEarly) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) kt_op[j][dt] = read_kt(j, dt);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       if (need_mask) {  // keys past the end or above the diagonal: S = -inf, P = 0
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -191,22 +218,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         bf16x8_t b;
 #pragma unroll
         for (int t = 0; t < 8; ++t) b[t] = (__bf16)dp[8 * j + t];
-        const __bf16* kb = Kb + (ks * 32 + j * 16) * D;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(kb + trk[0][dt]));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(kb + trk[1][dt]));
-          const bf16x4_t x = __builtin_bit_cast(bf16x4_t, lo), y = __builtin_bit_cast(bf16x4_t, hi);
-          bf16x8_t a;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            a[t] = x[t];
-            a[4 + t] = y[t];
-          }
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[dt], 0, 0, 0);
-        }
+        for (int dt = 0; dt < NDT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kEarly ? kt_op[j][dt] : read_kt(j, dt), b,
+                                                            acc[dt], 0, 0, 0);
       }
     }
   };
