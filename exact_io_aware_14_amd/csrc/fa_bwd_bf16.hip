@@ -233,7 +233,6 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    if (qt + 2 < nqt) issue_q(qt + 2, Qi, Gi, Li, Ei);
     const int qb0 = qt * C::BQ;
 
     // S = Q K^T and dP = dO V^T: queries on rows, this wave's keys on lanes; the
@@ -274,6 +273,8 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       for (int t = kk * TPK; t < kk * TPK + TPK; ++t) read_tr(t);
 #pragma unroll
       for (int t = kk * LPK; t < kk * LPK + LPK; ++t) read_le(t);
+      // tile qt+2 starts loading once the first products are under way
+      if (kk == 1 && qt + 2 < nqt) issue_q(qt + 2, Qi, Gi, Li, Ei);
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_v_ready(s, dp);
