@@ -49,9 +49,9 @@ SWEEP_HEADER = """# HBM traffic against sequence length — 16 heads, d=128, bf1
 
 Commands, from the repository root on one MI355X (`TMPDIR=/tmp`):
 
-    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/sweep/fetch -o p -- python -u bench.py --sweep-run
-    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/sweep/write -o p -- python -u bench.py --sweep-run
-    python -m exact_io_aware_14_amd.traffic gpurun_out/traffic --sweep gpurun_out/sweep
+    rocprofv3 --pmc FETCH_SIZE -f csv -d {sweep}/fetch -o p -- python -u bench.py --sweep-run
+    rocprofv3 --pmc WRITE_SIZE -f csv -d {sweep}/write -o p -- python -u bench.py --sweep-run
+    python -m exact_io_aware_14_amd.traffic {dir} --sweep {sweep}
 
 Counters scaled by the calibration of profiles/traffic.json.  FETCH_SIZE and WRITE_SIZE count
 the L2's requests to the memory fabric, so K/V re-reads that miss the per-XCD 4 MB L2 but hit the
@@ -60,7 +60,8 @@ each kernel must read and write once (forward Q, K, V, O; dK/dV pass Q, K, V, dO
 Q, K, V, dO, dQ), lse/D vectors left out.  A materialised score matrix would grow 16x from the
 first row to the last; the ratio staying flat is the linear traffic of the tiled method
 ("FlashAttention and online softmax", "HBM traffic").  At N = 16384 (B = 1) one head's K and V
-(8 MB together) alone exceed an XCD's 4 MB L2, and the re-reads show up as the 1.4-1.5x ratio.  Source hash: `{hash}`.
+(8 MB together) alone exceed an XCD's 4 MB L2, and the re-reads show up as the 1.4-1.5x ratio.  Source hashes
+(forward, dK/dV pass, dQ pass): {hash}.
 
 """
 
@@ -189,7 +190,9 @@ def main(argv=None) -> int:
             cal = json.load(f)["calibration"]
         table = sweep(args.sweep, cal["fetch_scale"], cal["write_scale"])
         with open(SWEEP_OUT, "w") as f:
-            f.write(SWEEP_HEADER.format(hash=source_hash()) + table + "\n")
+            hashes = ", ".join(f"`{source_hash(k)}`" for k in ("fwd_kernel", "bwd_main_kernel", "bwd_dq_kernel"))
+            f.write(SWEEP_HEADER.format(hash=hashes, dir=args.dir.rstrip("/"), sweep=args.sweep.rstrip("/"))
+                    + table + "\n")
         print(table)
         return 0
     s = summarize(args.dir, args.workload)
