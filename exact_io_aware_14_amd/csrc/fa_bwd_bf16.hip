@@ -254,10 +254,10 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       if (t & 1) bq[j][dt] = v;
       else bg[j][dt] = v;
     };
-    auto read_le = [&](int t) {  // t < 4: lse rows 8t + 4g + 0..3; else D rows
-      const int b = t & 3;
-      const float4 x = *reinterpret_cast<const float4*>((t < 4 ? Lc : Ec) + 8 * b + 4 * g);
-      float* dst = t < 4 ? lv : dvv;
+    auto read_le = [&](int t) {  // rows 8(t/2) + 4g + 0..3: lse for even t, D for odd t,
+      const int b = t >> 1;        // in the order the softmax below consumes them
+      const float4 x = *reinterpret_cast<const float4*>(((t & 1) ? Ec : Lc) + 8 * b + 4 * g);
+      float* dst = (t & 1) ? dvv : lv;
       dst[4 * b] = x.x, dst[4 * b + 1] = x.y, dst[4 * b + 2] = x.z, dst[4 * b + 3] = x.w;
     };
 #pragma unroll
