@@ -278,6 +278,11 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_v_ready(s, dp);
+    // All of this phase's LDS reads (transposed operands, lse, D) are waited for here,
+    // before the next tile's row reads below are issued: those are inline assembly the
+    // compiler does not count, so a wait it places later for one of this phase's reads
+    // would also wait for them.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
     // Keys past the end and, on tiles crossing the diagonal, keys above it: S = -inf,
     // so P = 2^-inf = 0 and dS = 0.  Only those tiles pay for the per-element test.
@@ -295,6 +300,21 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     // ALUs and by reads of the next tile's rows; sched_barrier keeps that interleave.
     constexpr int NSTEP = 2 * NDT, EPS = 16 / NSTEP;  // product pairs; elements per pair
     constexpr int RPS = (NKK + NSTEP - 1) / NSTEP;    // row-operand steps read per pair
+    // Each slice's P and dS are pinned where they are computed (empty asm reading
+    // them): the compiler would otherwise sink the dS arithmetic and the bf16
+    // conversions below the last product, where they run with the matrix cores idle.
+    // The first query half's bf16 operands are formed as soon as this step's last
+    // product reading the previous half-0 operands is issued; the second half's after
+    // the loop.
+    auto to_bf16 = [&](int j) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        pa[j][t] = (__bf16)s[8 * j + t];
+        da[j][t] = (__bf16)dp[8 * j + t];
+      }
+      asm volatile("" : "+v"(pa[j]), "+v"(da[j]));
+    };
+    static_assert(EPS * (NSTEP / 2) == 8 && NSTEP / 2 == NDT, "half 0 is done by slot NSTEP/2");
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
       const int j = i / NDT, dt = i % NDT;
@@ -302,21 +322,17 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       mma_a(dk[dt], da[j], bq[j][dt]);
 #pragma unroll
       for (int kk = i * RPS; kk < i * RPS + RPS && kk < NKK; ++kk) prefetch_rows(Qn, Gn, kk);
+      if (i == NSTEP / 2) to_bf16(0);  // products 0 .. NSTEP/2-1 read half 0
 #pragma unroll
       for (int r = i * EPS; r < i * EPS + EPS; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[r]));
         s[r] = p;
         dp[r] = p * (dp[r] - dvv[r]);
+        asm volatile("" : "+v"(s[r]), "+v"(dp[r]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        pa[j][t] = (__bf16)s[8 * j + t];
-        da[j][t] = (__bf16)dp[8 * j + t];
-      }
+    to_bf16(1);
     valu_ready(pa[0], pa[1], da[0], da[1]);  // read by the next step's products
   };
 
