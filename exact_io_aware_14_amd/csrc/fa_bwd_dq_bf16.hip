@@ -200,12 +200,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
           for (int dt = 0; dt < NDT; ++dt) kt_op[j][dt] = read_kt(j, dt);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (need_mask) {  // keys past the end or above the diagonal: S = -inf, P = 0
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + ks * 32 + crow(g, r);
-          s[r] = ((key >= N) | (causal & (key > myq)) | ((window > 0) & (key <= myq - window))) ? -INFINITY : s[r];
-        }
+      if (need_mask) {  // keys past the end, above the diagonal or below the window: P = 0
+        const int hi = causal ? min(myq, N - 1) : N - 1;
+        const int lo = window > 0 ? myq - window + 1 : 0;
+        mask_rows<GEN>(s, g, k0 + ks * 32, lo, hi);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {

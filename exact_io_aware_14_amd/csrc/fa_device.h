@@ -208,6 +208,23 @@ __device__ __forceinline__ void valu_ready(bf16x8_t& a, bf16x8_t& b, bf16x8_t& c
   asm volatile("s_nop 3" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }
 
+// Accumulator elements whose row index base + crow(g, r) lies outside [lo, hi] become
+// -inf.  crow(g, r) = 4g + off(r) with off(r) = 8(r/4) + r%4 a constant per register, so
+// each bound is one compare against a per-lane threshold; CHECK_LO = false drops the
+// lower bound.  |lo|, |hi| and base stay well inside int range at every call.
+template <bool CHECK_LO>
+__device__ __forceinline__ void mask_rows(f32x16_t& s, int g, int base, int lo, int hi) {
+  const int tlo = lo - base - 4 * g, thi = hi - base - 4 * g;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int off = 8 * (r >> 2) + (r & 3);
+    const bool dead = (off > thi) || (CHECK_LO && off < tlo);
+    s[r] = dead ? -INFINITY : s[r];
+  }
+}
+// Upper bound meaning "no upper bound" for mask_rows (leaves room for base + 4g).
+constexpr int kNoHi = 0x3fffffff;
+
 constexpr float kLog2e = 1.4426950408889634f;
 // Start value of the running max: finite, so that exp2((m_old - m_new) * c) and
 // s * c - m * c never form -inf - (-inf) while a row has seen no visible key.

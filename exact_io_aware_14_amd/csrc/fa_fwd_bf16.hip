@@ -215,15 +215,11 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
 
     const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw) ||
                            (window > 0 && k0 <= qw + 31 - window);
-    if (need_mask) {
+    if (need_mask) {  // keys past the end, above the diagonal or below the window
+      const int hi = causal ? min(myq, N - 1) : N - 1;
+      const int lo = window > 0 ? myq - window + 1 : 0;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + ks * 32 + crow(g, r);
-          if (key >= N || (causal && key > myq) || (window > 0 && key <= myq - window))
-            s[ks][r] = -INFINITY;
-        }
+      for (int ks = 0; ks < NKS; ++ks) mask_rows<GEN>(s[ks], g, k0 + ks * 32, lo, hi);
     }
 
     // Online softmax: tile max, lazily moved reference, p = 2^(s*c - mref*c).
