@@ -65,9 +65,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = id / nqb;
-  int qb = id - bh * nqb;
-  if (causal) qb = nqb - 1 - qb;  // longest query blocks of a head first
+  int bh = id / nqb, qb = id - bh * nqb;
+  if (causal) heavy_first(id, nqb, gridDim.x / nqb, bh, qb);  // longest query blocks first
   int base, N;  // first row and length of this (batch, head)
   seq_rows(sm, bh, Nmax, base, N);
   const size_t head = (size_t)base * D;

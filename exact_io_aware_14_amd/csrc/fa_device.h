@@ -132,6 +132,22 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
   return (id % kXcd) * (n / kXcd) + id / kXcd;
 }
 
+// Logical work id -> (unit, tile) when a unit's tiles differ in cost (causal: the last
+// query block of a head costs the most).  Units are taken in pairs, and within a pair
+// tiles go heaviest first, alternating between the two units.  An XCD's contiguous range
+// of ids then works on about two units at a time (their K/V stay in its L2), and the
+// heaviest tiles of every pair start before its light ones, so the grid does not end
+// with a few CUs finishing heavy tiles while the rest idle.  Ids cover nunits * nt.
+__device__ __forceinline__ void heavy_first(int id, int nt, int nunits, int& unit, int& tile) {
+  constexpr int G = 2;
+  const int group = id / (G * nt);
+  const int within = id - group * G * nt;
+  const int gs = min(G, nunits - group * G);  // the last group may hold one unit
+  const int rank = within / gs;
+  unit = group * G + (within - rank * gs);
+  tile = nt - 1 - rank;
+}
+
 // Rows of one (batch, head) unit of work.  Dense: [B, H, N, d], unit bh = b*H + h
 // owns rows bh*N .. bh*N + N-1.  Variable length (cu != null): tensors are packed
 // head-major [H, T, d] with sequence b in rows cu[b] .. cu[b+1]-1 of every head, and
