@@ -133,20 +133,24 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
 }
 
 // Logical work id -> (unit, tile) when a unit's tiles differ in cost (causal: the last
-// query block of a head costs the most).  Units are taken in pairs, and within a pair
-// tiles go heaviest first, alternating between the two units.  An XCD's contiguous range
-// of ids then works on about two units at a time (their K/V stay in its L2), and the
-// heaviest tiles of every pair start before its light ones, so the grid does not end
-// with a few CUs finishing heavy tiles while the rest idle.  Ids cover nunits * nt.
-__device__ __forceinline__ void heavy_first(int id, int nt, int nunits, int& unit, int& tile) {
-  constexpr int G = 2;
+// query block of a head costs the most).  Units are taken in groups of G, and within a
+// group tiles go heaviest first, alternating over the group's units.  With G = 2 an
+// XCD's contiguous range of ids works on about two units at a time and the heaviest tiles
+// of every pair start before its light ones, so the grid does not end with a few CUs
+// finishing heavy tiles while the rest idle; G = 1 is plain unit-by-unit order (heaviest
+// tile of each unit first).  Ids cover nunits * nt.
+__device__ __forceinline__ void heavy_first(int id, int nt, int nunits, int G, int& unit, int& tile) {
   const int group = id / (G * nt);
   const int within = id - group * G * nt;
-  const int gs = min(G, nunits - group * G);  // the last group may hold one unit
+  const int gs = min(G, nunits - group * G);  // the last group may hold fewer units
   const int rank = within / gs;
   unit = group * G + (within - rank * gs);
   tile = nt - 1 - rank;
 }
+// Units per group for heavy_first: pairs while two units' K and V (2 * N * D bf16 each)
+// fit an XCD's 4 MiB L2 beside other traffic; past that, pairing doubles the K/V re-reads
+// that miss it, and unit-by-unit order is better.
+__device__ __forceinline__ int heavy_group(int N, int D) { return (long long)N * D <= 4096 * 128 ? 2 : 1; }
 
 // Rows of one (batch, head) unit of work.  Dense: [B, H, N, d], unit bh = b*H + h
 // owns rows bh*N .. bh*N + N-1.  Variable length (cu != null): tensors are packed
