@@ -104,8 +104,12 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = id / nkb;
-  const int kb = id - bh * nkb;
+  int bh = id / nkb, kb = id - bh * nkb;
+  if (causal) {  // the first key blocks see the most query tiles: heaviest first
+    int t;
+    heavy_first(id, nkb, gridDim.x / nkb, heavy_group(Nmax, D), bh, t);
+    kb = nkb - 1 - t;
+  }
   int base, N;  // first row and length of this (batch, head)
   seq_rows(sm, bh, Nmax, base, N);
   const size_t head = (size_t)base * D;

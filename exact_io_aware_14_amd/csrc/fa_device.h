@@ -147,10 +147,14 @@ __device__ __forceinline__ void heavy_first(int id, int nt, int nunits, int G, i
   unit = group * G + (within - rank * gs);
   tile = nt - 1 - rank;
 }
-// Units per group for heavy_first: pairs while two units' K and V (2 * N * D bf16 each)
-// fit an XCD's 4 MiB L2 beside other traffic; past that, pairing doubles the K/V re-reads
-// that miss it, and unit-by-unit order is better.
-__device__ __forceinline__ int heavy_group(int N, int D) { return (long long)N * D <= 4096 * 128 ? 2 : 1; }
+// Units per group for heavy_first: as many as keep the group's K and V (2 * N * D bf16
+// per unit) within about 4 MiB, an XCD's L2 (1 to 8): two heads of 4096 x 128, eight of
+// 2048 x 64.  Larger groups balance small grids (few blocks per CU, where the longest
+// blocks set the time); past one head per group the extra K/V re-reads miss L2 for no gain.
+__device__ __forceinline__ int heavy_group(int N, int D) {
+  const long long nd = (long long)N * D;
+  return nd >= (1 << 20) ? 1 : (int)min(8LL, (1LL << 20) / nd);
+}
 
 // Rows of one (batch, head) unit of work.  Dense: [B, H, N, d], unit bh = b*H + h
 // owns rows bh*N .. bh*N + N-1.  Variable length (cu != null): tensors are packed
