@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   int bh = id / nkb, kb = id - bh * nkb;
   if (causal) {  // the first key blocks see the most query tiles: heaviest first
     int t;
-    heavy_first(id, nkb, gridDim.x / nkb, heavy_group(Nmax, D), bh, t);
+    heavy_first(id, nkb, gridDim.x / nkb, GEN ? 1 : heavy_group(Nmax, D), bh, t);
     kb = nkb - 1 - t;
   }
   int base, N;  // first row and length of this (batch, head)

@@ -151,6 +151,8 @@ __device__ __forceinline__ void heavy_first(int id, int nt, int nunits, int G, i
 // per unit) within about 4 MiB, an XCD's L2 (1 to 8): two heads of 4096 x 128, eight of
 // 2048 x 64.  Larger groups balance small grids (few blocks per CU, where the longest
 // blocks set the time); past one head per group the extra K/V re-reads miss L2 for no gain.
+// Variable-length batches keep groups of one: their units differ in length, and grouping
+// measured slower there.
 __device__ __forceinline__ int heavy_group(int N, int D) {
   const long long nd = (long long)N * D;
   return nd >= (1 << 20) ? 1 : (int)min(8LL, (1LL << 20) / nd);

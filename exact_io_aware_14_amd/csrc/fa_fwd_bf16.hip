@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
   const int g = lane >> 5, l32 = lane & 31;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   int bh = id / nqb, qb = id - bh * nqb;
-  if (causal) heavy_first(id, nqb, gridDim.x / nqb, heavy_group(Nmax, D), bh, qb);  // longest first
+  if (causal) heavy_first(id, nqb, gridDim.x / nqb, GEN ? 1 : heavy_group(Nmax, D), bh, qb);  // longest first
   int base, N;  // first row and length of this (batch, head)
   seq_rows(sm, bh, Nmax, base, N);
   const size_t head = (size_t)base * D;
