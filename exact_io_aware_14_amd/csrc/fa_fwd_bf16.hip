@@ -200,8 +200,9 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     };
     // Wave priority 1 while the wave issues its products, 0 during its softmax: when
     // both waves of a SIMD are ready, the one feeding the matrix cores goes first, and
-    // the other's vector work fills in, which pushes the two into opposite phases.
-    __builtin_amdgcn_s_setprio(1);
+    // the other's vector work fills in, which pushes the two into opposite phases.  (The
+    // general variant measured slightly slower with it and keeps a flat priority.)
+    if constexpr (!GEN) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kk = 0; kk < AHEAD; ++kk) read_k(kk);
 #pragma unroll
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     }
 
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(0);
+    if constexpr (!GEN) __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw) ||
                            (window > 0 && k0 <= qw + 31 - window);
     if (need_mask) {  // keys past the end, above the diagonal or below the window
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
       }
 
     // O^T += V^T P^T
-    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!GEN) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
