@@ -119,8 +119,8 @@ __device__ __forceinline__ void dma16(const void* base, unsigned voff, const voi
   const unsigned long long sbase = ((unsigned long long)hi << 32) | lo;
   const unsigned m0 = __builtin_amdgcn_readfirstlane(
       (unsigned)(unsigned long long)(const __attribute__((address_space(3))) void*)lds_wave);
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-               : "memory", "m0");
+  // M0 (the LDS destination) is bound as an operand, so the compiler sets it itself.
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
 // Block id -> logical work id.  Consecutive workgroup ids are spread round robin
@@ -197,14 +197,6 @@ __device__ __forceinline__ void seq_rows(const SeqMap& m, int bh, int Nmax, int&
 //     v_accvgpr_write: 4 (the documented need is 2).
 // Dependent MFMAs (one accumulating into the result of an earlier one) need no
 // wait states of their own.
-// acc = a * b (first product of a chain); acc in VGPRs, b in AGPRs.
-__device__ __forceinline__ void mma_v_first(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
-}
-// acc += a * b; acc in VGPRs, b in AGPRs.
-__device__ __forceinline__ void mma_v(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
-}
 // acc += a * b; acc in AGPRs, a and b in VGPRs.
 __device__ __forceinline__ void mma_a(f32x16_t& acc, const bf16x8_t& a, const bf16x8_t& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
@@ -248,8 +240,6 @@ __device__ __forceinline__ void mask_rows(f32x16_t& s, int g, int base, int lo, 
     s[r] = dead ? -INFINITY : s[r];
   }
 }
-// Upper bound meaning "no upper bound" for mask_rows (leaves room for base + 4g).
-constexpr int kNoHi = 0x3fffffff;
 
 constexpr float kLog2e = 1.4426950408889634f;
 // Start value of the running max: finite, so that exp2((m_old - m_new) * c) and
