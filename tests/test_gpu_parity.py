@@ -221,6 +221,37 @@ def test_bwd_stages_equal_fa_bwd(dev):
     check_grad("bf16", dq2, f64(dq1), "dQ", "stages")
 
 
+def test_calls_run_on_the_current_stream(dev):
+    """The binding enqueues on torch's current stream.  On a side stream (default
+    priority), a chain of large matrix products and then a copy into q and dO are
+    queued ahead of fa.fwd / fa.bwd.  Kernels launched on any other stream would start
+    before the copy lands and read zeros.  Results must equal those of the same calls on
+    the default stream, bit for bit."""
+    w = Workload("stream", 1, 2, 700, 128, True, "bf16", True, seed=5)
+    say("[stream] fwd + bwd queued behind a copy on a side stream")
+    x = make_inputs(w)
+    q, k, v, o_ref, lse_ref = gpu_fwd(x, w, dev)
+    do = x["do"].to(dev)
+    dq_ref, dk_ref, dv_ref = fa.bwd(q, k, v, o_ref, do, lse_ref, w.scale, True)
+    qs, dos = torch.zeros_like(q), torch.zeros_like(do)
+    a = torch.randn(4096, 4096, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(side):
+        for _ in range(8):  # keeps the side stream busy for several milliseconds
+            torch.mm(a, a, out=b)
+            torch.mm(b, b, out=a)
+        qs.copy_(q)
+        dos.copy_(do)
+        o, lse = fa.fwd(qs, k, v, w.scale, True)
+        dq, dk, dv = fa.bwd(qs, k, v, o, dos, lse, w.scale, True)
+    side.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    assert torch.equal(dq, dq_ref) and torch.equal(dk, dk_ref) and torch.equal(dv, dv_ref)
+
+
 @pytest.mark.timeout(600)
 def test_very_long_sequence(dev):
     """One head of 131072 tokens, d = 128, causal, bf16 (eight times a long-context
