@@ -204,7 +204,7 @@ def test_memory_stays_linear_long_context(dev):
 
 
 def test_bwd_stages_equal_fa_bwd(dev):
-    """fa_bwd_preprocess + fa_bwd_main + fa_bwd_finalize reproduce fa_bwd."""
+    """fa_bwd_preprocess + fa_bwd_main + fa_bwd_dq reproduce fa_bwd."""
     w = Workload("stages", 1, 3, 500, 128, True, "bf16", True, seed=7)
     say("[stages] bwd in three calls vs one")
     x = make_inputs(w)
