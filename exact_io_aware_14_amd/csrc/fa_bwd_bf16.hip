@@ -1,9 +1,9 @@
 // fa_bwd_bf16.hip -- the bf16 dK/dV pass of the backward, tuned for gfx950.
 //
 // Method ("FlashAttention and online softmax", ML Systems Lesson 4, "Backward pass:
-// recompute instead of store"): one workgroup per block of 128 keys (32 per wave),
-// K_j and V_j in registers, dK_j and dV_j accumulated in registers, query tiles of
-// 32 rows streamed; per tile
+// recompute instead of store"): one workgroup per block of keys (32 per wave at
+// d = 128, two blocks of 32 per wave at d = 64), K_j and V_j in registers, dK_j and dV_j
+// accumulated in registers, query tiles of 32 rows streamed; per tile
 //   S = Q_i K_j^T, P = exp2(S*scale*log2e - lse_i*log2e),  dP = dO_i V_j^T,
 //   dS = P o (dP - D_i),  dV_j += P^T dO_i,  dK_j += dS^T Q_i.
 // dQ is computed by its own query-stationary pass (fa_bwd_dq_bf16.hip), which
@@ -20,7 +20,8 @@
 // * S = Q K^T and dP = dO V^T put keys on the lane columns of the accumulators, so
 //   P^T and dS^T feed dV and dK as A operands straight from registers.
 // * One wave per SIMD (K, V, dK and dV alone hold 192 registers per lane at
-//   d = 128, all in AGPRs), so the overlap comes from inside the wave: the loop is
+//   d = 128, and as many for the two key blocks of a wave at d = 64, all in AGPRs), so
+//   the overlap comes from inside the wave: the loop is
 //   software pipelined.  Step i starts the S and dP products of tile i from Q/dO
 //   rows already in AGPRs; while they run it reads tile i-1's dO and Q transposed
 //   and tile i's lse and D; then tile i-1's dV/dK products alternate with slices of
@@ -38,7 +39,11 @@ template <int D>
 struct BwdFast {
   static constexpr int NW = 4;
   static constexpr int NT = 64 * NW;
-  static constexpr int BKV = 32 * NW;  // keys per workgroup
+  // 32-key blocks per wave: at d = 64, K, V, dK and dV of two blocks fit the registers
+  // that one block takes at d = 128, and every Q/dO operand read from LDS then feeds
+  // the products of both.
+  static constexpr int KB = D == 64 ? 2 : 1;
+  static constexpr int BKV = 32 * KB * NW;  // keys per workgroup
   static constexpr int BQ = 32;        // query rows per streamed tile (== kRowPad)
   static constexpr int CPR = D / 8;    // 16-byte chunks per row
   static constexpr int QTILE = BQ * D;
@@ -116,8 +121,8 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   const size_t hpad = (size_t)bh * Npad;
   const int k0 = kb * C::BKV;
   if (k0 >= N) return;  // a short sequence of a variable-length batch: no keys here
-  const int kw = k0 + w * 32;
-  const int mykey = kw + l32;
+  constexpr int KB = C::KB;
+  const int kw = k0 + w * 32 * KB;  // this wave's first key
 
   // --- direct-load source offsets ------------------------------------------------
   // Row-major swizzled tiles: chunk slot s = r*CPR + p holds logical chunk p ^ f(r).
@@ -167,35 +172,42 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     }
 
   // --- K and V of this wave's keys as B operands (natural k order) in registers --
-  bf16x8_t kop[NKK], vop[NKK];
+  bf16x8_t kop[KB][NKK], vop[KB][NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    if (mykey < N) {
-      const int off = (mykey - k0) * D + kk * 16 + g * 8;  // from the block's first key
-      kop[kk] = *reinterpret_cast<const bf16x8_t*>(K + head + (size_t)k0 * D + off);
-      vop[kk] = *reinterpret_cast<const bf16x8_t*>(V + head + (size_t)k0 * D + off);
-    } else {
+  for (int b = 0; b < KB; ++b)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        kop[kk][t] = (__bf16)0.0f;
-        vop[kk][t] = (__bf16)0.0f;
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int key = kw + 32 * b + l32;
+      if (key < N) {
+        const int off = (key - k0) * D + kk * 16 + g * 8;  // from the block's first key
+        kop[b][kk] = *reinterpret_cast<const bf16x8_t*>(K + head + (size_t)k0 * D + off);
+        vop[b][kk] = *reinterpret_cast<const bf16x8_t*>(V + head + (size_t)k0 * D + off);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          kop[b][kk][t] = (__bf16)0.0f;
+          vop[b][kk][t] = (__bf16)0.0f;
+        }
       }
     }
-  }
 
   // K and V only ever feed the matrix cores, which read A/B operands from AGPRs as
   // well; keeping them there leaves the VGPRs for operand prefetch.
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) asm volatile("s_nop 3" : "+a"(kop[kk]), "+a"(vop[kk]));
+  for (int b = 0; b < KB; ++b)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) asm volatile("s_nop 3" : "+a"(kop[b][kk]), "+a"(vop[b][kk]));
   // dK^T, dV^T accumulators in AGPRs (written by v_accvgpr_write: 4 wait states
   // before the first product accumulates into them).
-  f32x16_t dk[NDT], dv[NDT];
+  f32x16_t dk[KB][NDT], dv[KB][NDT];
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt) {
-    dk[dt] = zero16();
-    dv[dt] = zero16();
-    asm volatile("s_nop 3" : "+a"(dk[dt]), "+a"(dv[dt]));
-  }
+  for (int b = 0; b < KB; ++b)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      dk[b][dt] = zero16();
+      dv[b][dt] = zero16();
+      asm volatile("s_nop 3" : "+a"(dk[b][dt]), "+a"(dv[b][dt]));
+    }
   const float c = scale * kLog2e;
   // query tiles of this sequence (its padded rows hold lse = +inf: P = 0 there) ...
   int nqt = (N + C::BQ - 1) / C::BQ;
@@ -205,14 +217,16 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
 
   // P^T and dS^T of the previous tile, as bf16 A operands (j = 0, 1 query halves).
   // They start at zero, so the first step's dV/dK products add nothing.
-  bf16x8_t pa[2], da[2];
+  bf16x8_t pa[KB][2], da[KB][2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int b = 0; b < KB; ++b)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      pa[j][t] = (__bf16)0.0f;
-      da[j][t] = (__bf16)0.0f;
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        pa[b][j][t] = (__bf16)0.0f;
+        da[b][j][t] = (__bf16)0.0f;
+      }
   // Q and dO rows of the next tile (A operands of its S and dP), read one step ahead
   // straight into AGPRs: the S and dP products of a step then start right after its
   // barrier, and these reads run under the previous step's dV/dK products.
@@ -244,7 +258,7 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     // products go the step's other operand reads: tile qt-1's dO and Q transposed
     // (B operands of its dV/dK) and tile qt's lse and D, so those LDS round trips
     // start at once and run under the products instead of after them.
-    f32x16_t s, dp;
+    f32x16_t s[KB], dp[KB];
     bf16x8_t bg[2][NDT], bq[2][NDT];
     float lv[16], dvv[16];
     constexpr int NTR = 4 * NDT;        // transposed 16-byte operands to read
@@ -266,12 +280,15 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     };
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      if (kk == 0) {
-        mma_v_first_aa(s, aq[0], kop[0]);
-        mma_v_first_aa(dp, ag[0], vop[0]);
-      } else {
-        mma_v_aa(s, aq[kk], kop[kk]);
-        mma_v_aa(dp, ag[kk], vop[kk]);
+#pragma unroll
+      for (int b = 0; b < KB; ++b) {
+        if (kk == 0) {
+          mma_v_first_aa(s[b], aq[0], kop[b][0]);
+          mma_v_first_aa(dp[b], ag[0], vop[b][0]);
+        } else {
+          mma_v_aa(s[b], aq[kk], kop[b][kk]);
+          mma_v_aa(dp[b], ag[kk], vop[b][kk]);
+        }
       }
 #pragma unroll
       for (int t = kk * TPK; t < kk * TPK + TPK; ++t) read_tr(t);
@@ -281,7 +298,9 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       if (kk == 1 && qt + 2 < nqt) issue_q(qt + 2, Qi, Gi, Li, Ei);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mfma_v_ready(s, dp);
+    mfma_v_ready(s[KB - 1], dp[KB - 1]);
+#pragma unroll
+    for (int b = 0; b < KB - 1; ++b) asm volatile("" : "+v"(s[b]), "+v"(dp[b]));  // after the wait states
     // All of this phase's LDS reads (transposed operands, lse, D) are waited for here,
     // before the next tile's row reads below are issued: those are inline assembly the
     // compiler does not count, so a wait it places later for one of this phase's reads
@@ -290,19 +309,24 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
 
     // Keys past the end and, on tiles crossing the diagonal, keys above it: S = -inf,
     // so P = 2^-inf = 0 and dS = 0.  Only those tiles pay for the per-element test.
-    if ((kw + 32 > N) || (causal && kw + 31 > qb0) || (window > 0 && qb0 + 31 >= kw + window)) {
+    if ((kw + 32 * KB > N) || (causal && kw + 32 * KB - 1 > qb0) ||
+        (window > 0 && qb0 + 31 >= kw + window)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int q = qb0 + crow(g, r);
-        const bool dead = (mykey >= N) | (causal & (mykey > q)) | ((window > 0) & (q - mykey >= window));
-        s[r] = dead ? -INFINITY : s[r];
+      for (int b = 0; b < KB; ++b) {
+        const int key = kw + 32 * b + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int q = qb0 + crow(g, r);
+          const bool dead = (key >= N) | (causal & (key > q)) | ((window > 0) & (q - key >= window));
+          s[b][r] = dead ? -INFINITY : s[b][r];
+        }
       }
     }
 
     // The previous tile's dV/dK products (accumulating in AGPRs), each followed by
     // elements of this tile's P = 2^(s*c - lse2) and dS = P (dP - D) on the vector
     // ALUs and by reads of the next tile's rows; sched_barrier keeps that interleave.
-    constexpr int NSTEP = 2 * NDT, EPS = 16 / NSTEP;  // product pairs; elements per pair
+    constexpr int NSTEP = 2 * NDT * KB, EPS = 16 * KB / NSTEP;  // product pairs; elements per pair
     constexpr int RPS = (NKK + NSTEP - 1) / NSTEP;    // row-operand steps read per pair
     // Each slice's P and dS are pinned where they are computed (empty asm reading
     // them): the compiler would otherwise sink the dS arithmetic and the bf16
@@ -312,32 +336,40 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     // the loop.
     auto to_bf16 = [&](int j) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        pa[j][t] = (__bf16)s[8 * j + t];
-        da[j][t] = (__bf16)dp[8 * j + t];
+      for (int b = 0; b < KB; ++b) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          pa[b][j][t] = (__bf16)s[b][8 * j + t];
+          da[b][j][t] = (__bf16)dp[b][8 * j + t];
+        }
+        asm volatile("" : "+v"(pa[b][j]), "+v"(da[b][j]));
       }
-      asm volatile("" : "+v"(pa[j]), "+v"(da[j]));
     };
-    static_assert(EPS * (NSTEP / 2) == 8 && NSTEP / 2 == NDT, "half 0 is done by slot NSTEP/2");
+    // Pair i multiplies query half j = i / (KB*NDT) of key block (i / NDT) % KB; element e
+    // is row 8 * (e / (8*KB)) + e % 8 of key block (e / 8) % KB, so the first NSTEP/2
+    // pairs both read and (by their end) compute exactly query half 0.
+    static_assert(EPS * (NSTEP / 2) == 8 * KB && NSTEP / 2 == NDT * KB, "half 0 is done by slot NSTEP/2");
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
-      const int j = i / NDT, dt = i % NDT;
-      mma_a(dv[dt], pa[j], bg[j][dt]);
-      mma_a(dk[dt], da[j], bq[j][dt]);
+      const int j = i / (NDT * KB), b = (i / NDT) % KB, dt = i % NDT;
+      mma_a(dv[b][dt], pa[b][j], bg[j][dt]);
+      mma_a(dk[b][dt], da[b][j], bq[j][dt]);
 #pragma unroll
       for (int kk = i * RPS; kk < i * RPS + RPS && kk < NKK; ++kk) prefetch_rows(Qn, Gn, kk);
       if (i == NSTEP / 2) to_bf16(0);  // products 0 .. NSTEP/2-1 read half 0
 #pragma unroll
-      for (int r = i * EPS; r < i * EPS + EPS; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lv[r]));
-        s[r] = p;
-        dp[r] = p * (dp[r] - dvv[r]);
-        asm volatile("" : "+v"(s[r]), "+v"(dp[r]));
+      for (int e = i * EPS; e < i * EPS + EPS; ++e) {
+        const int b = (e / 8) % KB, r = 8 * (e / (8 * KB)) + e % 8;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lv[r]));
+        s[b][r] = p;
+        dp[b][r] = p * (dp[b][r] - dvv[r]);
+        asm volatile("" : "+v"(s[b][r]), "+v"(dp[b][r]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     to_bf16(1);
-    valu_ready(pa[0], pa[1], da[0], da[1]);  // read by the next step's products
+#pragma unroll
+    for (int b = 0; b < KB; ++b) valu_ready(pa[b][0], pa[b][1], da[b][0], da[b][1]);  // read next step
   };
 
   // Prologue: tiles qt0 and qt0+1 loading, then tile qt0's rows.  The first step reads
@@ -377,29 +409,36 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       for (int dt = 0; dt < NDT; ++dt) {
         const bf16x8_t bg = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
         const bf16x8_t bq = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
-        mma_a(dv[dt], pa[j], bg);
-        mma_a(dk[dt], da[j], bq);
+#pragma unroll
+        for (int b = 0; b < KB; ++b) {
+          mma_a(dv[b][dt], pa[b][j], bg);
+          mma_a(dk[b][dt], da[b][j], bq);
+        }
       }
   }
   // No direct load or prefetch read may still be in flight when the wave ends.
   __builtin_amdgcn_s_waitcnt(0x0070);
 
   // MFMA results in AGPRs: 16 wait states before v_accvgpr_read may take them.
-  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dk[0]), "+a"(dv[0]));
+  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dk[0][0]), "+a"(dv[0][0]));
 #pragma unroll
-  for (int dt = 1; dt < NDT; ++dt) asm volatile("" : "+a"(dk[dt]), "+a"(dv[dt]));
+  for (int b = 0; b < KB; ++b)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dk[b][dt]), "+a"(dv[b][dt]));
   // dK (scaled) and dV: lane = dim column, register = key row.
 #pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
+  for (int b = 0; b < KB; ++b)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kw + crow(g, r);
-      if (key < N) {
-        const size_t off = head + (size_t)k0 * D + ((key - k0) * D + dt * 32 + l32);
-        dK[off] = (__bf16)(dk[dt][r] * scale);
-        dV[off] = (__bf16)dv[dt][r];
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kw + 32 * b + crow(g, r);
+        if (key < N) {
+          const size_t off = head + (size_t)k0 * D + ((key - k0) * D + dt * 32 + l32);
+          dK[off] = (__bf16)(dk[b][dt][r] * scale);
+          dV[off] = (__bf16)dv[b][dt][r];
+        }
       }
-    }
 }
 
 template <int D, bool GEN>
