@@ -8,6 +8,7 @@ off (-packed-fp32-ops) for every HIP source.
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -40,8 +41,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, save_temps: str | None = None) -> str:
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        objs = []
-        for src in SOURCES:
+        def compile_one(src):
             obj = os.path.join(tmp, src.replace(".hip", ".o"))
             extra = []
             if save_temps:
@@ -61,7 +61,11 @@ def build(verbose: bool = False, save_temps: str | None = None) -> str:
                 raise RuntimeError(f"hipcc failed on {src}:\n{out}")
             if verbose and out.strip():
                 print(out)
-            objs.append(obj)
+            return obj
+
+        # one hipcc per source, run side by side (each is a separate process)
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 1)) as ex:
+            objs = list(ex.map(compile_one, SOURCES))
         tmp_lib = LIB + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+
 #include "fa.h"
 #include "fa_launch.h"
 
@@ -74,7 +75,7 @@ const char* fa_status_string(int status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128, dtype bf16 or fp32)";
-    case FA_ERR_LAUNCH: return "kernel launch failed";
+    case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     default: return "unknown status";
   }
 }
@@ -271,3 +272,4 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
 }
 
 }  // extern "C"
+

@@ -279,6 +279,7 @@ static hipError_t launch_pre_cfg(const BwdArgs& a) {
   constexpr int TPR = D / (16 / sizeof(T));
   const long long blocks = (prows * TPR + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  launch_begin();
   hipLaunchKernelGGL((bwd_pre_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)a.stream, (const T*)a.o, (const T*)a.dout, a.lse, a.Dvec, a.L2,
                      a.dqacc, a.N, a.Npad, prows, SeqMap{a.cu_seqlens, a.B, a.T});
@@ -291,6 +292,7 @@ static hipError_t launch_main_cfg(const BwdArgs& a) {
   const int nkb = (a.N + C::BKV - 1) / C::BKV;
   const long long grid = (long long)a.B * a.H * nkb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  launch_begin();
   hipLaunchKernelGGL((bwd_main_kernel<T, D, NW>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (const T*)a.dout, a.L2, a.Dvec, a.dqacc, (T*)a.dk, (T*)a.dv, a.N, a.Npad,
@@ -303,6 +305,7 @@ static hipError_t launch_fin_cfg(const BwdArgs& a) {
   const long long n4 = (long long)a.B * a.H * a.Npad * a.d / 4;
   const long long blocks = (n4 + 255) / 256;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  launch_begin();
   hipLaunchKernelGGL((dq_convert_kernel<T>), dim3((unsigned)blocks), dim3(256), 0,
                      (hipStream_t)a.stream, a.dqacc, (T*)a.dq, n4, a.N, a.Npad, a.d / 4,
                      a.scale, SeqMap{a.cu_seqlens, a.B, a.T});

@@ -447,6 +447,7 @@ static hipError_t launch_bwd_bf16_d(const BwdArgs& a) {
   const int nkb = (a.N + C::BKV - 1) / C::BKV;
   const long long grid = (long long)a.B * a.H * nkb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  launch_begin();
   hipLaunchKernelGGL((bwd_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dk,

@@ -272,6 +272,7 @@ hipError_t launch_partial_q(const SplitArgs& a) {
   const int chunk = (a.Nk + a.nsplit - 1) / a.nsplit;
   const long long grid = (long long)a.B * a.H * a.nsplit;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  launch_begin();
   hipLaunchKernelGGL((splitkv_partial_kernel<T, D, NQ>), dim3((unsigned)grid), dim3(kDecThreads), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v, a.o_part,
                      a.lse_part, a.B * a.H, a.Nq, a.Nk, chunk, a.nsplit, a.scale, a.causal);
@@ -297,6 +298,7 @@ hipError_t launch_splitkv_partial(const SplitArgs& a) {
 
 hipError_t launch_splitkv_merge(const MergeArgs& a) {
   if (a.nsplit > kMergeThreads) return hipErrorInvalidValue;
+  launch_begin();
   if (a.dtype == 0)
     hipLaunchKernelGGL((splitkv_merge_kernel<__bf16>), dim3((unsigned)a.rows), dim3(kMergeThreads), 0,
                        (hipStream_t)a.stream, a.o_part, a.lse_part, (__bf16*)a.o, a.lse, a.rows,

@@ -253,6 +253,7 @@ static hipError_t launch_fwd_cfg(const FwdArgs& a) {
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const long long grid = (long long)a.B * a.H * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  launch_begin();
   hipLaunchKernelGGL((fwd_kernel<T, D, BC, NW, QT>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const T*)a.q, (const T*)a.k, (const T*)a.v,
                      (T*)a.o, a.lse, a.N, a.scale, a.causal, nqb, SeqMap{a.cu_seqlens, a.B, a.T},

@@ -325,6 +325,7 @@ static hipError_t launch_fwd_bf16_d(const FwdArgs& a) {
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const long long grid = (long long)a.B * a.H * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  launch_begin();
   hipLaunchKernelGGL((fwd_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (__bf16*)a.o, a.lse, a.N, a.scale, a.causal, nqb,

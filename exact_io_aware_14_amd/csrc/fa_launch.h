@@ -8,6 +8,11 @@ namespace fa {
 
 enum { kBF16 = 0, kFP32 = 1 };
 
+// Called right before each kernel launch: takes an error that earlier, unrelated HIP
+// calls left in this thread's error slot out of it, so that the hipGetLastError()
+// after the launch reports only what the launch itself caused.
+inline void launch_begin() { (void)hipGetLastError(); }
+
 // Per-head row padding of the backward's D and lse workspace vectors: every
 // backward query tile (32 rows) reads whole padded vectors.
 constexpr int kRowPad = 32;

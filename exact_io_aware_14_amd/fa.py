@@ -104,6 +104,38 @@ def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
+def _out(t, shape, dtype, device, name):
+    """A caller-supplied output buffer, checked before the library sees it: the C ABI
+    cannot see buffer sizes, so a short or mistyped buffer would be written past its
+    end on the device.  Returns ``t``."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} of shape {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name} must live on {device}, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _workspace(ws, device, need: int):
+    """A caller-supplied workspace: contiguous device memory of at least ``need`` bytes."""
+    if not isinstance(ws, torch.Tensor) or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {device}")
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace holds {ws.numel() * ws.element_size()} bytes, {need} needed")
+    return ws
+
+
+def _grads(grads, like):
+    if grads is None:
+        return tuple(torch.empty_like(like) for _ in range(3))
+    if len(grads) != 3:
+        raise ValueError("grads must be (dq, dk, dv)")
+    return tuple(_out(g, like.shape, like.dtype, like.device, n) for g, n in zip(grads, ("dq", "dk", "dv")))
+
+
 def workspace_bytes(B: int, H: int, N: int, d: int, dtype: torch.dtype) -> int:
     return int(lib().fa_bwd_workspace_bytes(B, H, N, d, _DTYPES[dtype]))
 
@@ -114,8 +146,9 @@ def fwd(q, k, v, scale: float | None = None, causal: bool = False, out=None, lse
     B, H, N, d = _dims(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _out(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+         else _out(lse, (B, H, N), torch.float32, q.device, "lse"))
     st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                       B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype], _stream(q.device))
     if st != FA_OK:
@@ -130,14 +163,12 @@ def bwd(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
     B, H, N, d = _dims(q)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor")
+    _out(lse, (B, H, N), torch.float32, q.device, "lse")
     nbytes = workspace_bytes(B, H, N, d, q.dtype)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    if grads is None:
-        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    dq, dk, dv = grads
+    _workspace(workspace, q.device, nbytes)
+    dq, dk, dv = _grads(grads, q)
     st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -153,7 +184,9 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
     list of three callables so a caller can time or interleave them."""
     _check_same(q, k, v, o, do)
     B, H, N, d = _dims(q)
-    dq, dk, dv = grads
+    _out(lse, (B, H, N), torch.float32, q.device, "lse")
+    _workspace(workspace, q.device, workspace_bytes(B, H, N, d, q.dtype))
+    dq, dk, dv = _grads(grads, q)
     L, dt, st = lib(), _DTYPES[q.dtype], _stream(q.device)
     wp, wn = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     sc, ca = float(scale), int(bool(causal))
@@ -178,7 +211,7 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
     return [pre, main, dqs]
 
 
-def _ex_dims(q, cu_seqlens, max_seqlen):
+def _ex_dims(q, cu_seqlens, max_seqlen, validate=True):
     """(B, H, N, total, d, lse shape, cu pointer) of a dense or packed call."""
     if cu_seqlens is None:
         B, H, N, d = _dims(q)
@@ -191,19 +224,36 @@ def _ex_dims(q, cu_seqlens, max_seqlen):
     if max_seqlen is None:
         raise ValueError("max_seqlen is required with cu_seqlens")
     H, T, d = (int(x) for x in q.shape)
+    if validate:
+        # The library reads the table on the device and cannot reject it; checked here
+        # on a host copy (one device-to-host transfer), so that a table outside the
+        # rules of fa_fwd_ex fails loudly instead of giving wrong rows.
+        cu = cu_seqlens.cpu().tolist()
+        if len(cu) < 2 or cu[0] != 0 or cu[-1] != T:
+            raise ValueError(f"cu_seqlens must run from 0 to total = {T}")
+        lens = [b - a for a, b in zip(cu, cu[1:])]
+        if min(lens) < 0:
+            raise ValueError("cu_seqlens must be non-decreasing")
+        if max(lens) > int(max_seqlen):
+            raise ValueError(f"a sequence of {max(lens)} tokens exceeds max_seqlen = {max_seqlen}")
     return int(cu_seqlens.numel()) - 1, H, int(max_seqlen), T, d, (H, T), cu_seqlens.data_ptr()
 
 
 def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, window: int = 0,
-           cu_seqlens=None, max_seqlen: int | None = None, out=None, lse=None):
+           cu_seqlens=None, max_seqlen: int | None = None, out=None, lse=None,
+           validate: bool = True):
     """Forward with a sliding window and/or variable-length packed sequences
-    ([H, total, d] with int32 cu_seqlens [B+1]); see fa_fwd_ex in include/fa.h."""
+    ([H, total, d] with int32 cu_seqlens [B+1]); see fa_fwd_ex in include/fa.h.
+    ``validate`` checks cu_seqlens on a host copy first (0 = cu[0] <= ... <= cu[B] =
+    total, every length <= max_seqlen); a caller that guarantees that may pass False
+    to skip the device-to-host transfer."""
     _check_same(q, k, v)
-    B, H, N, T, d, lshape, cu = _ex_dims(q, cu_seqlens, max_seqlen)
+    B, H, N, T, d, lshape, cu = _ex_dims(q, cu_seqlens, max_seqlen, validate)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty(lshape, dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _out(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty(lshape, dtype=torch.float32, device=q.device) if lse is None
+         else _out(lse, lshape, torch.float32, q.device, "lse"))
     st = lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(), cu,
                          B, H, N, T, d, float(scale), int(bool(causal)), int(window),
                          _DTYPES[q.dtype], _stream(q.device))
@@ -213,20 +263,19 @@ def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, window: in
 
 
 def bwd_ex(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False, window: int = 0,
-           cu_seqlens=None, max_seqlen: int | None = None, workspace=None, grads=None):
+           cu_seqlens=None, max_seqlen: int | None = None, workspace=None, grads=None,
+           validate: bool = True):
     """Backward of :func:`fwd_ex` (same layout and arguments)."""
     _check_same(q, k, v, o, do)
-    B, H, N, T, d, lshape, cu = _ex_dims(q, cu_seqlens, max_seqlen)
+    B, H, N, T, d, lshape, cu = _ex_dims(q, cu_seqlens, max_seqlen, validate)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    if lse.dtype != torch.float32 or tuple(lse.shape) != lshape or not lse.is_contiguous():
-        raise ValueError(f"lse must be a contiguous float32 {lshape} tensor")
+    _out(lse, lshape, torch.float32, q.device, "lse")
+    nbytes = workspace_bytes(B, H, N, d, q.dtype)
     if workspace is None:
-        workspace = torch.empty(max(workspace_bytes(B, H, N, d, q.dtype), 1), dtype=torch.uint8,
-                                device=q.device)
-    if grads is None:
-        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
-    dq, dk, dv = grads
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, q.device, nbytes)
+    dq, dk, dv = _grads(grads, q)
     st = lib().fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
                          lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(), cu,
@@ -259,11 +308,13 @@ def fwd_splitkv(q, k, v, num_splits: int, scale: float | None = None, causal: bo
     B, H, Nq, Nk, d = _check_decode(q, k, v)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    l = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = torch.empty_like(q) if out is None else _out(out, q.shape, q.dtype, q.device, "out")
+    l = (torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None
+         else _out(lse, (B, H, Nq), torch.float32, q.device, "lse"))
+    n = splitkv_workspace_bytes(B, H, Nq, d, num_splits)
     if workspace is None:
-        n = splitkv_workspace_bytes(B, H, Nq, d, num_splits)
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, q.device, n)
     st = lib().fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), l.data_ptr(),
                               B, H, Nq, Nk, d, float(scale), int(bool(causal)), int(num_splits),
                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -280,8 +331,10 @@ def fwd_partial(q, k, v, num_splits: int, scale: float | None = None, causal: bo
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     S = int(num_splits)
-    op = torch.empty((S, B, H, Nq, d), dtype=torch.float32, device=q.device) if o_part is None else o_part
-    lp = torch.empty((S, B, H, Nq), dtype=torch.float32, device=q.device) if lse_part is None else lse_part
+    op = (torch.empty((S, B, H, Nq, d), dtype=torch.float32, device=q.device) if o_part is None
+          else _out(o_part, (S, B, H, Nq, d), torch.float32, q.device, "o_part"))
+    lp = (torch.empty((S, B, H, Nq), dtype=torch.float32, device=q.device) if lse_part is None
+          else _out(lse_part, (S, B, H, Nq), torch.float32, q.device, "lse_part"))
     st = lib().fa_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), op.data_ptr(), lp.data_ptr(),
                               B, H, Nq, Nk, d, float(scale), int(bool(causal)), S,
                               _DTYPES[q.dtype], _stream(q.device))
@@ -301,8 +354,15 @@ def merge(o_part, lse_part, dtype: torch.dtype = torch.float32, out=None, lse=No
         raise ValueError("o_part [S, ..., d] and lse_part [S, ...] disagree")
     S, d = int(o_part.shape[0]), int(o_part.shape[-1])
     rows = int(lse_part.numel() // max(S, 1))
-    o = torch.empty(tuple(o_part.shape[1:]), dtype=dtype, device=o_part.device) if out is None else out
-    l = torch.empty(tuple(lse_part.shape[1:]), dtype=torch.float32, device=o_part.device) if lse is None else lse
+    if o_part.device.type != "cuda" or lse_part.device != o_part.device:
+        raise ValueError("partials must live on one GPU")
+    if dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {dtype} (bf16 or float32)")
+    oshape, lshape = tuple(o_part.shape[1:]), tuple(lse_part.shape[1:])
+    o = (torch.empty(oshape, dtype=dtype, device=o_part.device) if out is None
+         else _out(out, oshape, dtype, o_part.device, "out"))
+    l = (torch.empty(lshape, dtype=torch.float32, device=o_part.device) if lse is None
+         else _out(lse, lshape, torch.float32, o_part.device, "lse"))
     st = lib().fa_merge(o_part.data_ptr(), lse_part.data_ptr(), o.data_ptr(), l.data_ptr(),
                         S, rows, d, _DTYPES[dtype], _stream(o_part.device))
     if st != FA_OK:

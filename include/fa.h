@@ -38,7 +38,9 @@
  *                          softmax_scale not finite and > 0, causal not 0 or 1,
  *                          or a workspace shorter than fa_bwd_workspace_bytes();
  *   FA_ERR_UNSUPPORTED  -- d not 64 or 128, or an unknown dtype;
- *   FA_ERR_LAUNCH       -- the HIP runtime rejected a kernel launch.
+ *   FA_ERR_LAUNCH       -- the HIP runtime rejected a kernel launch (an error
+ *                          that earlier, unrelated HIP calls left pending on the
+ *                          calling thread is cleared first and never reported).
  * There is no fallback path of any kind: an unsupported request fails loudly
  * ("FlashAttention from Scratch", section "Pitfalls that turn into incidents").
  *
@@ -137,9 +139,11 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
  *       pass cu_seqlens instead of padded batches).  Tensors are then packed
  *       head-major, [H, total, d] (sequence b of head h in rows cu[b] .. cu[b+1]-1),
  *       lse is [H, total] float32, N is the longest length (max_seqlen) and every
- *       sequence attends only within itself.  The table is read on the device and not
- *       checked: a table outside these rules gives undefined rows (it can never make a
- *       kernel access memory outside the tensors) and lengths above N are cut to N.
+ *       sequence attends only within itself.  The table is the caller's contract: the
+ *       kernels read it on the device and this call cannot check it without a
+ *       device-to-host copy.  A table outside these rules (including a length above N)
+ *       gives wrong rows without an error, though never an access outside the
+ *       tensors; the Python binding checks the table on a host copy before the call.
  *   window : 0 = no window.  W >= 1 (requires causal = 1): a causal band, query i
  *       sees key j iff i - W < j <= i ("FlashAttention and online softmax", "Where it
  *       shows up": sliding-window masks with tile skipping); tiles outside the band

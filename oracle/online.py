@@ -19,10 +19,11 @@ noted):
 * ``merge`` is the formula of section "Merging two partial results", in its stable
   form lse = max + log(1 + exp(-|lse_A - lse_B|)), with the empty-set rules stated
   there (lse = -inf has weight 0; both empty gives o = 0, lse = -inf).
-* ``tiled_forward`` is the tiled forward pass of "The online softmax theorem /
-  The tiled forward pass" (query tile kept, K/V tiles streamed, causal tiles above
-  the diagonal skipped as in "Causal masks and FlashAttention-3").  It is the
-  method's schedule, used to show that the schedule reaches the oracle's result.
+* ``tiled_forward`` is the tiled forward pass of "The online softmax theorem"
+  (blocks of queries and of keys, a running reference value, denominator and
+  numerator per query row, blocks wholly above the causal diagonal skipped as in
+  "Causal masks and FlashAttention-3"), run in either loop order of section "HBM
+  traffic".  It shows that the block schedule reaches the oracle's result.
 """
 from __future__ import annotations
 
@@ -111,37 +112,85 @@ def merge(o_a, lse_a, o_b, lse_b):
     return wa * o_a + wb * o_b, lse
 
 
-def tiled_forward(Q, K, V, scale: float, Br: int = 16, Bc: int = 16, causal: bool = False):
-    """Tiled forward pass for one head (Q, K, V: [N, d]); returns (O, lse).
+class _RowState:
+    """Running state of a set of query rows under the online-softmax theorem: the
+    reference value ``ref`` each row's weights are measured against (the largest
+    score seen so far, -inf before any visible key), the denominator ``den`` (sum of
+    the weights) and the numerator ``num`` (weight-times-value sum, [rows, d])."""
 
-    Per query tile: m = -inf, l = 0, acc = 0; for each K/V tile (skipping tiles that
-    lie wholly above the causal diagonal) compute the score tile, update m, rescale
-    l and acc by exp(m_old - m_new), add the tile's terms; divide once at the end.
+    def __init__(self, rows: int, d: int):
+        self.ref = np.full(rows, -np.inf)
+        self.den = np.zeros(rows)
+        self.num = np.zeros((rows, d))
+
+    def fold(self, sel, scores, values):
+        """Fold a block of scores (hidden pairs = -inf) of the rows ``sel`` and their
+        value rows into the state.  Rows whose block is wholly hidden keep their state
+        (the theorem's empty-block case: never -inf - (-inf))."""
+        old = self.ref[sel]
+        top = scores.max(axis=1)
+        seen = top > -np.inf
+        new = np.where(seen, np.maximum(old, top), old)
+        # weight of the old state under the new reference: 0 if it was empty
+        keep = np.zeros_like(old)
+        had = old > -np.inf
+        keep[had] = np.exp(old[had] - new[had])
+        w = np.zeros_like(scores)
+        w[seen] = np.exp(scores[seen] - new[seen][:, None])
+        self.den[sel] = keep * self.den[sel] + w.sum(axis=1)
+        self.num[sel] = keep[:, None] * self.num[sel] + w @ values
+        self.ref[sel] = new
+
+    def result(self):
+        """(O, lse): O = num / den and lse = ref + log den; empty rows give O = 0,
+        lse = -inf."""
+        live = self.den > 0.0
+        O = np.zeros_like(self.num)
+        O[live] = self.num[live] / self.den[live][:, None]
+        lse = np.full(self.den.shape, -np.inf)
+        lse[live] = self.ref[live] + np.log(self.den[live])
+        return O, lse
+
+
+def _hidden(q_lo: int, nq: int, k_lo: int, nk: int, causal: bool):
+    """[nq, nk] boolean table of the pairs the causal rule hides (key index above the
+    query index) in the block of queries q_lo.. and keys k_lo..; None if none is."""
+    if not causal or k_lo + nk - 1 <= q_lo:
+        return None
+    first_hidden = np.arange(q_lo, q_lo + nq) + 1 - k_lo  # per row: first hidden column
+    return np.arange(nk)[None, :] >= first_hidden[:, None]
+
+
+def tiled_forward(Q, K, V, scale: float, Br: int = 16, Bc: int = 16, causal: bool = False,
+                  order: str = "kv_outer"):
+    """Tiled forward pass of one head (Q, K, V: [N, d]) by the online-softmax theorem;
+    returns (O, lse).
+
+    ``order="kv_outer"`` is the schedule of the original paper's algorithm as the
+    pages describe it (section "HBM traffic": outer loop over K/V blocks, inner loop
+    over query blocks, the per-row running state kept for all N rows between visits).
+    ``order="q_outer"`` is the FlashAttention-2 schedule of the same section (each
+    query block's state finished before the next block starts).  Either way a block
+    pair that the causal rule hides entirely is never touched ("Causal masks and
+    FlashAttention-3"), and O is divided by the denominator once at the end.
     """
     Q, K, V = (np.asarray(t, dtype=np.float64) for t in (Q, K, V))
     N, d = Q.shape
-    O, lse = np.zeros_like(Q), np.empty(N)
-    for i in range(0, N, Br):
-        q = Q[i:i + Br]
-        r = q.shape[0]
-        m, l, acc = np.full(r, -np.inf), np.zeros(r), np.zeros((r, d))
-        for j in range(0, N, Bc):
-            if causal and j > i + r - 1:
-                break
-            s = scale * (q @ K[j:j + Bc].T)
-            if causal:
-                rows = np.arange(i, i + r)[:, None]
-                cols = np.arange(j, j + s.shape[1])[None, :]
-                s = np.where(cols <= rows, s, -np.inf)
-            m_new = np.maximum(m, s.max(axis=1))
-            live = m_new > -np.inf
-            m_ref = np.where(live, m_new, 0.0)
-            f = np.where(m == -np.inf, 0.0, np.exp(np.where(live, m, 0.0) - m_ref))
-            p = np.exp(s - m_ref[:, None])
-            p[~live] = 0.0
-            l = f * l + p.sum(axis=1)
-            acc = f[:, None] * acc + p @ V[j:j + Bc]
-            m = m_new
-        O[i:i + r] = acc / l[:, None]
-        lse[i:i + r] = m + np.log(l)
-    return O, lse
+    q_blocks = [(a, min(Br, N - a)) for a in range(0, N, Br)]
+    k_blocks = [(a, min(Bc, N - a)) for a in range(0, N, Bc)]
+    if order == "kv_outer":
+        pairs = [(qb, kb) for kb in k_blocks for qb in q_blocks]
+    elif order == "q_outer":
+        pairs = [(qb, kb) for qb in q_blocks for kb in k_blocks]
+    else:
+        raise ValueError(f"unknown order {order!r}")
+    state = _RowState(N, d)
+    for (q_lo, nq), (k_lo, nk) in pairs:
+        if causal and k_lo > q_lo + nq - 1:
+            continue  # every key of the block lies above every query of the block
+        block = scale * (Q[q_lo:q_lo + nq] @ K[k_lo:k_lo + nk].T)
+        hide = _hidden(q_lo, nq, k_lo, nk, causal)
+        if hide is not None:
+            block[hide] = -np.inf
+        state.fold(slice(q_lo, q_lo + nq), block, V[k_lo:k_lo + nk])
+    return state.result()

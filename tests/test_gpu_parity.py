@@ -165,18 +165,13 @@ def test_invalid_arguments_fail_loudly(dev):
 def test_autograd_saves_linear_memory(dev):
     """What the fused method keeps for backward at N=1000, d=64, fp32: Q, K, V, O
     and the lse, 1,028,000 bytes ("FlashAttention and online softmax", section 5)."""
+    from saved_bytes import saved_storage_bytes
+
     say("[saved bytes] N=1000 d=64 fp32")
-    torch.manual_seed(0)
-    x = [torch.randn(1, 1, 1000, 64, device=dev, requires_grad=True) for _ in range(3)]
-    seen = {}
-
-    def pack(t):
-        seen[t.untyped_storage().data_ptr()] = t.untyped_storage().nbytes()
-        return t
-
-    with torch.autograd.graph.saved_tensors_hooks(pack, lambda t: t):
-        out = fa.attention(*x)
-    assert sum(seen.values()) == 1028000
+    gen = torch.Generator(device=dev).manual_seed(0)
+    x = [torch.randn(1, 1, 1000, 64, device=dev, generator=gen).requires_grad_() for _ in range(3)]
+    out = fa.attention(*x)
+    assert saved_storage_bytes(out) == 1028000
     out.sum().backward()
     assert all(torch.isfinite(t.grad).all().item() for t in x)
 
@@ -275,3 +270,44 @@ def test_very_long_sequence(dev):
                                             w.scale, True)
         check_fwd("bf16", o[:, :, i:i + 1], lse[:, :, i:i + 1], O_ref, lse_ref, f"row {i}")
     say(f"  {len(rows)} sampled rows match")
+
+
+def test_binding_rejects_bad_output_buffers(dev):
+    """Caller-supplied outputs of the wrong shape, dtype, device or layout raise
+    ValueError in the binding, before anything is enqueued (the C ABI cannot see
+    buffer sizes)."""
+    say("[errors] output buffers checked by the binding")
+    B, H, N, d = 1, 2, 64, 64
+    q = torch.randn(B, H, N, d, device=dev, dtype=torch.bfloat16)
+    o, lse = fa.fwd(q, q, q)
+    bad_outs = [torch.empty(B, H, N, d // 2, device=dev, dtype=torch.bfloat16),  # short
+                torch.empty(B, H, N, d, device=dev, dtype=torch.float32),       # dtype
+                torch.empty(B, H, N, d, dtype=torch.bfloat16),                  # host memory
+                torch.empty(B, H, d, N, device=dev, dtype=torch.bfloat16).transpose(2, 3)]
+    bad_lse = [torch.empty(B, H, device=dev), torch.empty(B, H, N, device=dev, dtype=torch.bfloat16),
+               torch.empty(B, H, N)]
+    for t in bad_outs:
+        with pytest.raises(ValueError):
+            fa.fwd(q, q, q, out=t)
+        with pytest.raises(ValueError):
+            fa.bwd(q, q, q, o, q, lse, grads=(torch.empty_like(q), t, torch.empty_like(q)))
+    for t in bad_lse:
+        with pytest.raises(ValueError):
+            fa.fwd(q, q, q, lse=t)
+        with pytest.raises(ValueError):
+            fa.bwd(q, q, q, o, q, t)
+    with pytest.raises(ValueError):  # workspace too short
+        fa.bwd(q, q, q, o, q, lse, workspace=torch.empty(16, dtype=torch.uint8, device=dev))
+    with pytest.raises(ValueError):  # fwd_ex output
+        fa.fwd_ex(q, q, q, causal=True, window=4, out=bad_outs[0])
+    qd = torch.randn(B, H, 1, d, device=dev, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # split-KV partials of the wrong shape
+        fa.fwd_partial(qd, q, q, 4, o_part=torch.empty(4, B, H, 1, d // 2, device=dev))
+    with pytest.raises(ValueError):
+        fa.fwd_partial(qd, q, q, 4, lse_part=torch.empty(4, B, H, device=dev))
+    op, lp = fa.fwd_partial(qd, q, q, 4)
+    with pytest.raises(ValueError):  # merge output of the wrong dtype / shape
+        fa.merge(op, lp, torch.bfloat16, out=torch.empty(B, H, 1, d, device=dev))
+    with pytest.raises(ValueError):
+        fa.merge(op, lp, torch.float32, lse=torch.empty(B, H, 2, device=dev))
+    torch.cuda.synchronize()

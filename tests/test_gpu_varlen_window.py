@@ -177,3 +177,20 @@ def test_ex_invalid_args(dev):
     r = fa.lib().fa_fwd_ex(qp.data_ptr(), qp.data_ptr(), qp.data_ptr(), qp.data_ptr(), raw.data_ptr(),
                            cu.data_ptr() + 2, 2, 1, 64, 64, 64, 0.125, 1, 0, fa.FA_DTYPE_BF16, 0)
     assert r == fa.FA_ERR_INVALID_ARG  # misaligned cu_seqlens
+
+
+def test_binding_checks_cu_seqlens(dev):
+    """A cu_seqlens table outside the rules (not from 0 to total, decreasing, or a
+    sequence longer than max_seqlen) raises ValueError in the binding, which checks a
+    host copy; the library itself cannot see the device table."""
+    T = 64
+    qp = torch.zeros((1, T, 64), dtype=torch.bfloat16, device=dev)
+    cu_dev = lambda v: torch.tensor(v, dtype=torch.int32, device=dev)
+    for cu, nmax in (([0, 10, 60], 64), ([1, 10, 64], 64), ([0, 40, 30, 64], 64), ([0, 50, 64], 32)):
+        with pytest.raises(ValueError):
+            fa.fwd_ex(qp, qp, qp, None, True, cu_seqlens=cu_dev(cu), max_seqlen=nmax)
+    o, lse = fa.fwd_ex(qp, qp, qp, None, True, cu_seqlens=cu_dev([0, 50, 64]), max_seqlen=50)
+    do = torch.zeros_like(qp)
+    with pytest.raises(ValueError):
+        fa.bwd_ex(qp, qp, qp, o, do, lse, None, True, cu_seqlens=cu_dev([0, 50, 64]), max_seqlen=49)
+    torch.cuda.synchronize()

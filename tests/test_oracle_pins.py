@@ -215,24 +215,27 @@ def test_lse_is_scipy_logsumexp():
             assert np.abs(lse[0, h] - logsumexp(S, axis=1)).max() < 1e-13
 
 
-def test_tiled_equals_naive():
+@pytest.mark.parametrize("order", ["kv_outer", "q_outer"])
+def test_tiled_equals_naive(order):
     """Lesson 4, section 5 'In code' (b): tiled forward = naive at N=100, d=32,
-    Br=Bc=16, with and without the causal mask, to 1e-12."""
+    Br=Bc=16, with and without the causal mask, to 1e-12 (both loop orders of
+    section "HBM traffic")."""
     rng = np.random.default_rng(0)
     Q, K, V = (rng.normal(size=(100, 32)) for _ in range(3))
     for causal in (False, True):
-        O1, l1 = tiled_forward(Q, K, V, 1 / math.sqrt(32), 16, 16, causal)
+        O1, l1 = tiled_forward(Q, K, V, 1 / math.sqrt(32), 16, 16, causal, order=order)
         O2, l2 = attention_fwd(Q[None, None], K[None, None], V[None, None], 1 / math.sqrt(32), causal)
         assert np.abs(O1 - O2[0, 0]).max() < 1e-12
         assert np.abs(l1 - l2[0, 0]).max() < 1e-12
 
 
+@pytest.mark.parametrize("order", ["kv_outer", "q_outer"])
 @pytest.mark.parametrize("Br,Bc", [(7, 5), (32, 64), (100, 3)])
-def test_tiled_equals_naive_other_tiles(Br, Bc):
+def test_tiled_equals_naive_other_tiles(Br, Bc, order):
     rng = np.random.default_rng(Br * Bc)
     Q, K, V = (rng.normal(size=(77, 16)) for _ in range(3))
     for causal in (False, True):
-        O1, l1 = tiled_forward(Q, K, V, 0.25, Br, Bc, causal)
+        O1, l1 = tiled_forward(Q, K, V, 0.25, Br, Bc, causal, order=order)
         O2, l2 = attention_fwd(Q[None, None], K[None, None], V[None, None], 0.25, causal)
         assert np.abs(O1 - O2[0, 0]).max() < 1e-12
         assert np.abs(l1 - l2[0, 0]).max() < 1e-12
