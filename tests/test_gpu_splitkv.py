@@ -125,6 +125,11 @@ def test_splitkv_invalid_args(dev):
         fa.fwd_partial(q1, k, k, 257)
     assert e.value.status == fa.FA_ERR_UNSUPPORTED
     small = torch.empty(16, dtype=torch.uint8, device=dev)
-    with pytest.raises(fa.FaError) as e:
+    with pytest.raises(ValueError):  # the binding checks the workspace's size first
         fa.fwd_splitkv(q1, k, k, 4, workspace=small)
-    assert e.value.status == fa.FA_ERR_INVALID_ARG
+    o = torch.empty_like(q1)
+    lse = torch.empty((1, 1, 4), dtype=torch.float32, device=dev)
+    st = fa.lib().fa_fwd_splitkv(q1.data_ptr(), k.data_ptr(), k.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                                 1, 1, 4, 20, 64, 0.125, 1, 4, small.data_ptr(), 16, fa.FA_DTYPE_BF16,
+                                 torch.cuda.current_stream().cuda_stream)
+    assert st == fa.FA_ERR_INVALID_ARG  # and so does the C ABI, before any launch
