@@ -3,6 +3,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -68,14 +69,15 @@ size_t split_part_bytes(int B, int H, int Nq, int d, int nsplit) {
 
 extern "C" {
 
-int fa_abi_version(void) { return (1 << 16) | 0; }
+int fa_abi_version(void) { return (1 << 16) | 1; }
 
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument";
     case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim must be 64 or 128, dtype bf16 or fp32)";
-    case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case FA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch or the scratch lookup";
+    case FA_ERR_TOO_LARGE: return "the call needs more scratch than fa_bwd_noalloc's fixed FA_NOALLOC_SCRATCH_BYTES";
     default: return "unknown status";
   }
 }
@@ -273,3 +275,56 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
 
 }  // extern "C"
 
+// ---- fa_bwd_noalloc: fa_bwd with a library-owned workspace ---------------------------
+// The workspace (D and lse*log2(e) vectors, plus the fp32 path's dQ accumulator) lives
+// in this file-scope device array instead of caller memory.  Each device the library
+// runs on holds its own copy from module load until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is handed to the
+// kernels.
+static __device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (looked up on the first call there).
+hipError_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                    int B, int H, int N, int d, float softmax_scale, int causal,
+                                    int dtype, void* stream) {
+  // The checks of fa_bwd with a stand-in workspace (aligned, large enough): they do not
+  // read it.
+  fa_status st = fa_bwd_check(q, k, v, o, dout, lse, dq, dk, dv, (const void*)256, (size_t)-1, B,
+                              H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (ws_bytes(B, H, N, d, dtype) > (size_t)FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return FA_ERR_LAUNCH;
+  // The preprocess writes every padded row of D and lse*log2(e) and clears the fp32
+  // accumulator, so nothing a previous call left in the scratch is read.
+  const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, softmax_scale,
+                                 causal, dtype, stream);
+  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}

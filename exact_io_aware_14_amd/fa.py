@@ -15,12 +15,13 @@ import torch
 
 __all__ = ["lib", "fwd", "bwd", "bwd_stages", "workspace_bytes", "attention", "FaError",
            "fwd_splitkv", "fwd_partial", "merge", "splitkv_workspace_bytes", "fwd_ex", "bwd_ex",
-           "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_LAUNCH",
+           "bwd_noalloc", "FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_LAUNCH",
+           "FA_ERR_TOO_LARGE",
            "FA_DTYPE_BF16", "FA_DTYPE_FP32", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_TOO_LARGE = 0, 1, 2, 3, 4
 FA_DTYPE_BF16, FA_DTYPE_FP32 = 0, 1
 
 _DTYPES = {torch.bfloat16: FA_DTYPE_BF16, torch.float32: FA_DTYPE_FP32}
@@ -73,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.fa_fwd_partial.restype = i
         L.fa_merge.argtypes = [vp, vp, vp, vp, i, i, i, i, vp]
         L.fa_merge.restype = i
+        L.fa_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, f, i, i, vp]
+        L.fa_bwd_noalloc.restype = i
         L.fa_status_string.argtypes = [i]
         L.fa_status_string.restype = ctypes.c_char_p
         L.fa_abi_version.argtypes = []
@@ -176,6 +179,25 @@ def bwd(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
                       _stream(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
+                grads=None):
+    """:func:`bwd` through fa_bwd_noalloc: no workspace, the library's fixed scratch
+    instead (calls on one GPU must not overlap; see include/fa.h)."""
+    _check_same(q, k, v, o, do)
+    B, H, N, d = _dims(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _out(lse, (B, H, N), torch.float32, q.device, "lse")
+    dq, dk, dv = _grads(grads, q)
+    st = lib().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                              lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                              B, H, N, d, float(scale), int(bool(causal)), _DTYPES[q.dtype],
+                              _stream(q.device))
+    if st != FA_OK:
+        raise FaError(st, "fa_bwd_noalloc")
     return dq, dk, dv
 
 

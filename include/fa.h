@@ -63,7 +63,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,
   FA_ERR_UNSUPPORTED = 2,
-  FA_ERR_LAUNCH = 3
+  FA_ERR_LAUNCH = 3,
+  FA_ERR_TOO_LARGE = 4 /* fa_bwd_noalloc only: the call does not fit its fixed scratch */
 } fa_status;
 
 typedef enum { FA_DTYPE_BF16 = 0, FA_DTYPE_FP32 = 1 } fa_dtype;
@@ -209,6 +210,29 @@ fa_status fa_fwd_partial(const void* q, const void* k, const void* v, float* o_p
  * alignment; INVALID_ARG for null pointers or sizes out of range. */
 fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* lse,
                    int num_splits, int rows, int d, int dtype, void* stream);
+
+/* ---- Backward without a workspace argument -------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): fa_bwd with the same arguments
+ * except the workspace, which here is a fixed array of FA_NOALLOC_SCRATCH_BYTES inside
+ * the library.  Each GPU the library runs on holds one such array from module load
+ * until the process ends; its address is looked up once per device, on the first
+ * call there.  The call allocates and frees nothing.
+ *   - It fits iff fa_bwd_workspace_bytes(B, H, N, d, dtype) <= FA_NOALLOC_SCRATCH_BYTES
+ *     (bf16: B*H*ceil32(N) <= 4M rows; fp32: B*H*ceil32(N)*(8 + 4d) bytes <= 32 MiB);
+ *     a larger call returns FA_ERR_TOO_LARGE before anything is enqueued.
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in time on one
+ *     GPU (different streams, threads or processes' shared contexts) race and give
+ *     undefined results; serialise them, e.g. on one stream.  Nothing a previous call
+ *     left in the array is read (the preprocess rewrites all of it that is used).
+ *   - `stream` must belong to the current device.
+ * Results equal fa_bwd's on the same inputs (bitwise for bf16).  Other errors as
+ * fa_bwd; FA_ERR_LAUNCH also if the scratch address cannot be obtained. */
+#define FA_NOALLOC_SCRATCH_BYTES (32u << 20)
+fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int N, int d, float softmax_scale, int causal,
+                         int dtype, void* stream);
 
 /* Host-only argument checks of fa_fwd / fa_bwd (same rules, same codes); they
  * touch no device and enqueue nothing.  Pointers are checked for null and

@@ -25,7 +25,7 @@ def test_exports_every_declared_symbol():
     names = declared_functions()
     assert set(names) >= {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_status_string",
                           "fa_fwd_check", "fa_bwd_check", "fa_abi_version", "fa_bwd_preprocess",
-                          "fa_bwd_main", "fa_bwd_dq"}
+                          "fa_bwd_main", "fa_bwd_dq", "fa_bwd_noalloc"}
     L = ctypes.CDLL(fa.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -33,7 +33,8 @@ def test_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     L = fa.lib()
-    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_LAUNCH):
+    for code in (fa.FA_OK, fa.FA_ERR_INVALID_ARG, fa.FA_ERR_UNSUPPORTED, fa.FA_ERR_LAUNCH,
+                 fa.FA_ERR_TOO_LARGE):
         assert L.fa_status_string(code) and L.fa_status_string(code) != b"unknown status"
     assert L.fa_status_string(99) == b"unknown status"
     assert L.fa_abi_version() >> 16 == 1
@@ -92,3 +93,22 @@ def test_entry_points_reject_before_touching_the_device():
     assert L.fa_fwd(P, P, P, P, P, 1, 1, 10, 96, 0.1, 0, 0, None) == fa.FA_ERR_UNSUPPORTED
     assert L.fa_fwd(None, P, P, P, P, 1, 1, 10, 64, 0.1, 0, 0, None) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd(P, P, P, P, P, P, P, P, P, P, 0, 1, 1, 10, 64, 0.1, 0, 0, None) == fa.FA_ERR_INVALID_ARG
+
+
+def test_noalloc_size_limit_is_checked_on_the_host():
+    """fa_bwd_noalloc refuses a call whose workspace would exceed its fixed scratch
+    (FA_NOALLOC_SCRATCH_BYTES, 32 MiB) before touching any device, and runs fa_bwd's
+    argument checks first."""
+    L = fa.lib()
+    limit = 32 << 20
+    assert "FA_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
+    B, H, N, d = 64, 64, 1056, 64  # bf16: 2 x 4.3M padded rows of 4 bytes
+    assert L.fa_bwd_workspace_bytes(B, H, N, d, 0) > limit
+    assert L.fa_bwd_workspace_bytes(64, 64, 1024, 64, 0) <= limit  # exactly 32 MiB fits
+    args = lambda B, H, N, d, dt: (P, P, P, P, P, P, P, P, P, B, H, N, d, 0.125, 1, dt, None)
+    assert L.fa_bwd_noalloc(*args(B, H, N, d, 0)) == fa.FA_ERR_TOO_LARGE
+    # fp32 adds a [B, H, Npad, d] accumulator: 4 x 32 x 1024 rows x 520 bytes > 32 MiB
+    assert L.fa_bwd_noalloc(*args(4, 32, 1024, 128, 1)) == fa.FA_ERR_TOO_LARGE
+    assert L.fa_bwd_noalloc(None, *args(1, 1, 64, 64, 0)[1:]) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_bwd_noalloc(*args(1, 1, 64, 96, 0)) == fa.FA_ERR_UNSUPPORTED
+    assert L.fa_status_string(fa.FA_ERR_TOO_LARGE) != b"unknown status"
