@@ -20,7 +20,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "to_f64",
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "draw_f32", "finish_inputs", "to_f64",
            "DecodeWorkload", "DECODE_WORKLOADS", "make_decode_inputs",
            "WINDOW_WORKLOADS", "VarlenWorkload", "VARLEN_WORKLOADS", "varlen_lengths",
            "make_varlen_inputs"]
@@ -69,22 +69,34 @@ def _round(x: np.ndarray, dtype: str) -> torch.Tensor:
     raise ValueError(f"unknown dtype {dtype!r}")
 
 
-def make_inputs(w: Workload, with_do: bool | None = None) -> dict:
-    """Draw the workload's tensors. Returns dict q, k, v[, do] of CPU torch tensors."""
+def draw_f32(w: Workload, with_do: bool | None = None) -> dict:
+    """The workload's float32 draws before any planting or rounding: dict q, k, v[, do]
+    of numpy arrays (the first steps of the recipe)."""
     if with_do is None:
         with_do = w.backward
     rng = np.random.default_rng(w.seed)
     shape = (w.B, w.H, w.N, w.d)
     names = ["q", "k", "v"] + (["do"] if with_do else [])
+    return {name: rng.standard_normal(shape, dtype=np.float32) for name in names}
+
+
+def finish_inputs(draws: dict, w: Workload) -> dict:
+    """The recipe's last steps on draws from draw_f32: scale the planted query row of
+    ``w.planted`` (on a copy of q), then round every tensor to ``w.dtype``."""
     out = {}
-    for name in names:
-        x = rng.standard_normal(shape, dtype=np.float32)
+    for name, x in draws.items():
         if name == "q" and w.planted is not None:
             b, h, row, factor = w.planted
             if b < w.B and h < w.H and row < w.N:
+                x = x.copy()
                 x[b, h, row, :] *= np.float32(factor)
         out[name] = _round(x, w.dtype)
     return out
+
+
+def make_inputs(w: Workload, with_do: bool | None = None) -> dict:
+    """Draw the workload's tensors. Returns dict q, k, v[, do] of CPU torch tensors."""
+    return finish_inputs(draw_f32(w, with_do), w)
 
 
 @dataclass(frozen=True)

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from exact_io_aware_14_amd import fa
-from exact_io_aware_14_amd.inputs import WORKLOADS, Workload, make_inputs, to_f64
+from exact_io_aware_14_amd.inputs import WORKLOADS, Workload, draw_f32, finish_inputs, make_inputs, to_f64
 from oracle import attention_bwd, attention_fwd
 from oracle.splitkv import attention_fwd_rect
 from parity import check_fwd, check_grad, f64
@@ -82,9 +82,12 @@ def _full(name):
 HEADS = {
     "tiny_fp32": [(0, 0)],
     "gpt2m_fwd": [(0, 0), (7, 15)],
-    "long_causal": [(0, 0), (3, 31)],
+    # 16 heads spread over the dispatch groups of two heads (b*H + h = 0, 9, 17, ... 127):
+    # both members of a pair, first and last groups, every batch
+    "long_causal": [(bh // 32, bh % 32) for bh in (0, 9, 17, 26, 34, 43, 51, 60, 68, 77, 85, 94,
+                                                   102, 111, 119, 127)],
     "train_step": [(0, 0), (3, 15)],
-    "long_context": [(0, 15)],
+    "long_context": [(0, 0), (0, 5), (0, 10), (0, 15)],
 }
 
 
@@ -133,6 +136,44 @@ def test_planted_row_exercises_rescaling(dev):
     O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, True)
     check_fwd("bf16", o[:, :, row:row + 1], lse[:, :, row:row + 1], O_ref[:, :, row:row + 1],
               lse_ref[:, :, row:row + 1], "planted")
+
+
+# Planted rows of the long causal layer (query row x 30 before rounding): the default
+# (0, 0, 2049), its neighbours across the 2048 tile boundary, the last row of the first
+# and last heads, and rows of other heads.  On such a nearly one-hot row dS = P (dP - D)
+# cancels two close numbers, and D = dO . O from the bf16 O is the largest error in dK.
+PLANTED = [(0, 0, 2049), (0, 0, 2047), (0, 0, 2048), (0, 0, 4095), (3, 31, 4095), (2, 5, 1023),
+           (0, 0, 63), (1, 9, 3000)]
+
+
+@pytest.mark.timeout(900)
+def test_planted_rows_full_size(dev):
+    """The long causal layer at full size with the planted row at each of PLANTED: every
+    output of the planted head against the oracle, to the bf16 bars (dK within 5e-2 of
+    its max-norm); the margins are printed."""
+    w0 = _full("long_causal")
+    draws = draw_f32(w0, with_do=True)
+    base = finish_inputs({n: draws[n] for n in ("k", "v", "do")}, w0)
+    k, v, do = (base[n].to(dev) for n in ("k", "v", "do"))
+    worst = 0.0
+    for (b, h, row) in PLANTED:
+        w = w0.with_(planted=(b, h, row, 30.0))
+        say(f"[planted] row {row} of head ({b},{h})")
+        xq = finish_inputs({"q": draws["q"]}, w)["q"]
+        q = xq.to(dev)
+        o, lse = fa.fwd(q, k, v, w.scale, True)
+        dq, dk, dv = fa.bwd(q, k, v, o, do, lse, w.scale, True)
+        torch.cuda.synchronize()
+        Q = to_f64(xq[b:b + 1, h:h + 1])
+        K, V, dO = (to_f64(base[n][b:b + 1, h:h + 1]) for n in ("k", "v", "do"))
+        O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, True)
+        check_fwd("bf16", o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], O_ref, lse_ref, f"planted {row}")
+        refs = attention_bwd(Q, K, V, dO, w.scale, True)
+        errs = {n: check_grad("bf16", G[b:b + 1, h:h + 1], R, n, f"planted ({b},{h},{row})")
+                for n, G, R in zip(("dQ", "dK", "dV"), (dq, dk, dv), refs)}
+        say(f"  dQ {errs['dQ']:.4f} dK {errs['dK']:.4f} dV {errs['dV']:.4f} (bar 0.05)")
+        worst = max(worst, errs["dK"])
+    say(f"[planted] worst dK relative error {worst:.4f}")
 
 
 def test_fwd_bitwise_deterministic(dev):
