@@ -135,6 +135,23 @@ static fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const v
                      B, H, N, d, fa::pad_rows(N), scale, causal, dtype, stream};
 }
 
+// The backward's launches.  bf16: the dQ pass with the preprocess folded in (it writes
+// D and lse*log2(e) for the dK/dV pass), then the dK/dV pass.  fp32: preprocess, dK/dV
+// pass (which adds the dQ contributions to the accumulator), dQ conversion.
+// `launches` selects a subset (bit 0: the first launch, bit 1: the second, bit 2: the
+// third), for callers that time them one by one.
+static fa_status run_bwd(const fa::BwdArgs& a, int launches = 7) {
+  if (a.dtype == FA_DTYPE_BF16) {
+    if ((launches & 1) && fa::launch_bwd_dq_pre_bf16(a) != hipSuccess) return FA_ERR_LAUNCH;
+    if ((launches & 2) && fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
+    return FA_OK;
+  }
+  if ((launches & 1) && fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if ((launches & 2) && fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
+  if ((launches & 4) && fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
+  return FA_OK;
+}
+
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
                  size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
@@ -144,10 +161,7 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   if (st != FA_OK) return st;
   const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, workspace, B, H, N, d,
                                  softmax_scale, causal, dtype, stream);
-  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
+  return run_bwd(a);
 }
 
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
@@ -183,6 +197,19 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
   const fa::BwdArgs a = bwd_args(q, k, v, nullptr, dout, nullptr, dq, nullptr, nullptr, workspace,
                                  B, H, N, d, softmax_scale, causal, dtype, stream);
   return fa::launch_bwd_dq(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+fa_status fa_bwd_dq_pre(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* workspace,
+                        size_t workspace_bytes, int B, int H, int N, int d, float softmax_scale,
+                        int causal, int dtype, void* stream) {
+  const fa_status st = fa_bwd_check(q, k, v, o, dout, lse, dq, dq, dq, workspace, workspace_bytes, B,
+                                    H, N, d, softmax_scale, causal, dtype);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, nullptr, nullptr, workspace, B, H, N, d,
+                                 softmax_scale, causal, dtype, stream);
+  return fa::launch_bwd_dq_pre_bf16(a) == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 size_t fa_splitkv_workspace_bytes(int B, int H, int Nq, int d, int num_splits) {
@@ -257,6 +284,17 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
                     size_t workspace_bytes, const int* cu_seqlens, int B, int H, int N, int total,
                     int d, float softmax_scale, int causal, int window, int dtype, void* stream) {
+  return fa_bwd_ex_launches(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                            cu_seqlens, B, H, N, total, d, softmax_scale, causal, window, dtype,
+                            FA_BWD_ALL_LAUNCHES, stream);
+}
+
+fa_status fa_bwd_ex_launches(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, const int* cu_seqlens, int B,
+                             int H, int N, int total, int d, float softmax_scale, int causal,
+                             int window, int dtype, int launches, void* stream) {
+  if (launches < 1 || launches > FA_BWD_ALL_LAUNCHES) return FA_ERR_INVALID_ARG;
   fa_status st = fa_bwd_check(q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, H,
                               N, d, softmax_scale, causal, dtype);
   if (st != FA_OK) return st;
@@ -267,10 +305,7 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o, 
   a.cu_seqlens = cu_seqlens;
   a.T = cu_seqlens ? total : 0;
   a.window = window;
-  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
+  return run_bwd(a, launches);
 }
 
 }  // extern "C"
@@ -323,8 +358,5 @@ extern "C" fa_status fa_bwd_noalloc(const void* q, const void* k, const void* v,
   // accumulator, so nothing a previous call left in the scratch is read.
   const fa::BwdArgs a = bwd_args(q, k, v, o, dout, lse, dq, dk, dv, ws, B, H, N, d, softmax_scale,
                                  causal, dtype, stream);
-  if (fa::launch_bwd_preprocess(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_main(a) != hipSuccess) return FA_ERR_LAUNCH;
-  if (fa::launch_bwd_dq(a) != hipSuccess) return FA_ERR_LAUNCH;
-  return FA_OK;
+  return run_bwd(a);
 }

@@ -42,10 +42,16 @@ __device__ __forceinline__ int dq_swz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
-template <int D, bool GEN>
+// PRE = true folds the backward's preprocess into this pass: each lane forms its own
+// row's D = dO . O and lse * log2(e) (the same products and the same summation tree as
+// bwd_pre_kernel, so the values are bit for bit those the preprocess would write), uses
+// them, and writes them to the workspace vectors (padding rows: D = 0, +inf) for the
+// dK/dV pass that runs next.  PRE = false reads them from the workspace.
+template <int D, bool GEN, bool PRE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
+    const __bf16* __restrict__ dO, float* __restrict__ L2, float* __restrict__ Dvec,
+    const __bf16* __restrict__ O, const float* __restrict__ LSE,
     __bf16* __restrict__ dQ, int Nmax, int Npad, float scale, int causal, int nqb, SeqMap sm_arg,
     int window_arg) {
   // GEN = false: dense tensors, no window; the general code folds away.
@@ -129,8 +135,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
       }
     }
   }
-  const float lse2 = L2[(size_t)bh * Npad + min(myq, Npad - 1)];  // +inf past N: P = 0
-  const float dval = Dvec[(size_t)bh * Npad + min(myq, Npad - 1)];
+  float lse2, dval;
+  if constexpr (PRE) {
+    // D: per 16-byte chunk p = 2 kk + g an fma chain over its 8 elements, then the
+    // butterfly over chunks (p ^ 8, 4, 2 within the lane's chunks, p ^ 1 across the
+    // half-waves): the order bwd_pre_kernel adds them in.
+    float part[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      part[kk] = 0.0f;
+      if (myq < N) {
+        const int off = (myq - q0) * D + kk * 16 + g * 8;
+        const bf16x8_t o8 = *reinterpret_cast<const bf16x8_t*>(O + head + (size_t)q0 * D + off);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) part[kk] = fmaf((float)o8[t], (float)gop[kk][t], part[kk]);
+      }
+    }
+#pragma unroll
+    for (int x = NKK / 2; x > 0; x >>= 1) {
+      float nxt[NKK];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) nxt[kk] = part[kk] + part[kk ^ x];
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) part[kk] = nxt[kk];
+    }
+    dval = part[0] + __shfl_xor(part[0], 32);
+    lse2 = myq < N ? LSE[(size_t)base + myq] * kLog2e : INFINITY;  // +inf past N: P = 0
+    if (myq >= N) dval = 0.0f;
+    if (g == 0 && myq < Npad) {
+      Dvec[(size_t)bh * Npad + myq] = dval;
+      L2[(size_t)bh * Npad + myq] = lse2;
+    }
+  } else {
+    lse2 = L2[(size_t)bh * Npad + min(myq, Npad - 1)];  // +inf past N: P = 0
+    dval = Dvec[(size_t)bh * Npad + min(myq, Npad - 1)];
+  }
 
   f32x16_t acc[NDT];
 #pragma unroll
@@ -247,26 +286,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   }
 }
 
-template <int D, bool GEN>
+template <int D, bool GEN, bool PRE>
 static hipError_t launch_dq_bf16_d(const BwdArgs& a) {
   using C = DqFast<D>;
   const int nqb = (a.N + C::BR - 1) / C::BR;
   const long long grid = (long long)a.B * a.H * nqb;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   launch_begin();
-  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
+  hipLaunchKernelGGL((bwd_dq_bf16_kernel<D, GEN, PRE>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
-                     (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dq,
-                     a.N, a.Npad, a.scale, a.causal, nqb, SeqMap{a.cu_seqlens, a.B, a.T},
-                     a.window);
+                     (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec,
+                     (const __bf16*)a.o, a.lse, (__bf16*)a.dq, a.N, a.Npad, a.scale, a.causal,
+                     nqb, SeqMap{a.cu_seqlens, a.B, a.T}, a.window);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dq_bf16(const BwdArgs& a) {
+template <bool PRE>
+static hipError_t launch_dq_bf16(const BwdArgs& a) {
   const bool gen = a.cu_seqlens != nullptr || a.window > 0;
-  if (a.d == 64) return gen ? launch_dq_bf16_d<64, true>(a) : launch_dq_bf16_d<64, false>(a);
-  if (a.d == 128) return gen ? launch_dq_bf16_d<128, true>(a) : launch_dq_bf16_d<128, false>(a);
+  if (a.d == 64) return gen ? launch_dq_bf16_d<64, true, PRE>(a) : launch_dq_bf16_d<64, false, PRE>(a);
+  if (a.d == 128) return gen ? launch_dq_bf16_d<128, true, PRE>(a) : launch_dq_bf16_d<128, false, PRE>(a);
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a) { return launch_dq_bf16<false>(a); }
+hipError_t launch_bwd_dq_pre_bf16(const BwdArgs& a) { return launch_dq_bf16<true>(a); }
 
 }  // namespace fa

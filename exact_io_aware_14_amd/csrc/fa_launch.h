@@ -79,5 +79,7 @@ hipError_t launch_bwd_main(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
 hipError_t launch_bwd_main_bf16(const BwdArgs& a);  // gfx950-tuned bf16 dK/dV pass
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a);    // gfx950-tuned bf16 dQ pass
+// bf16 dQ pass with the preprocess folded in: also writes D and lse*log2(e) (needs o, lse)
+hipError_t launch_bwd_dq_pre_bf16(const BwdArgs& a);
 
 }  // namespace fa

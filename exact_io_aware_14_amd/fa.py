@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_main.restype = i
         L.fa_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
         L.fa_bwd_dq.restype = i
+        L.fa_bwd_dq_pre.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i, vp]
+        L.fa_bwd_dq_pre.restype = i
         L.fa_fwd_check.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, f, i, i]
         L.fa_fwd_check.restype = i
         L.fa_bwd_check.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, f, i, i]
@@ -66,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.fa_bwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, i,
                                 i, vp]
         L.fa_bwd_ex.restype = i
+        L.fa_bwd_ex_launches.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f,
+                                         i, i, i, i, vp]
+        L.fa_bwd_ex_launches.restype = i
         L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
         L.fa_splitkv_workspace_bytes.restype = sz
         L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, i, vp]
@@ -201,9 +206,11 @@ def bwd_noalloc(q, k, v, o, do, lse, scale: float | None = None, causal: bool = 
     return dq, dk, dv
 
 
-def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
-    """The three stages of :func:`bwd` as separate calls (same result), returning a
-    list of three callables so a caller can time or interleave them."""
+def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads, fused: bool = False):
+    """The backward as separate calls (same result as :func:`bwd`), returned as a list of
+    callables so a caller can time or interleave them.  ``fused=False``: the three stages
+    fa_bwd_preprocess, fa_bwd_main, fa_bwd_dq.  ``fused=True``: the launches fa_bwd itself
+    makes (bf16: fa_bwd_dq_pre, then fa_bwd_main; fp32: the three stages)."""
     _check_same(q, k, v, o, do)
     B, H, N, d = _dims(q)
     _out(lse, (B, H, N), torch.float32, q.device, "lse")
@@ -230,6 +237,14 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads):
         if r != FA_OK:
             raise FaError(r, "fa_bwd_dq")
 
+    def dq_pre():
+        r = L.fa_bwd_dq_pre(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                            lse.data_ptr(), dq.data_ptr(), wp, wn, B, H, N, d, sc, ca, dt, st)
+        if r != FA_OK:
+            raise FaError(r, "fa_bwd_dq_pre")
+
+    if fused and q.dtype == torch.bfloat16:
+        return [dq_pre, main]
     return [pre, main, dqs]
 
 
@@ -286,8 +301,10 @@ def fwd_ex(q, k, v, scale: float | None = None, causal: bool = False, window: in
 
 def bwd_ex(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False, window: int = 0,
            cu_seqlens=None, max_seqlen: int | None = None, workspace=None, grads=None,
-           validate: bool = True):
-    """Backward of :func:`fwd_ex` (same layout and arguments)."""
+           validate: bool = True, launches: int = 7):
+    """Backward of :func:`fwd_ex` (same layout and arguments).  ``launches`` selects
+    which of the backward's kernel launches to enqueue (a bit mask in their order; see
+    fa_bwd_ex_launches in include/fa.h); the default runs all of them."""
     _check_same(q, k, v, o, do)
     B, H, N, T, d, lshape, cu = _ex_dims(q, cu_seqlens, max_seqlen, validate)
     if scale is None:
@@ -298,11 +315,11 @@ def bwd_ex(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
     _workspace(workspace, q.device, nbytes)
     dq, dk, dv = _grads(grads, q)
-    st = lib().fa_bwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                         lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                         workspace.data_ptr(), workspace.numel() * workspace.element_size(), cu,
-                         B, H, N, T, d, float(scale), int(bool(causal)), int(window),
-                         _DTYPES[q.dtype], _stream(q.device))
+    st = lib().fa_bwd_ex_launches(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), cu,
+                                  B, H, N, T, d, float(scale), int(bool(causal)), int(window),
+                                  _DTYPES[q.dtype], int(launches), _stream(q.device))
     if st != FA_OK:
         raise FaError(st, "fa_bwd_ex")
     return dq, dk, dv

@@ -56,8 +56,8 @@ Commands, from the repository root on one MI355X (`TMPDIR=/tmp`):
 Counters scaled by the calibration of profiles/traffic.json.  FETCH_SIZE and WRITE_SIZE count
 the L2's requests to the memory fabric, so K/V re-reads that miss the per-XCD 4 MB L2 but hit the
 256 MB last-level cache count here too.  Algorithmic bytes: the tensors
-each kernel must read and write once (forward Q, K, V, O; dK/dV pass Q, K, V, dO, dK, dV; dQ pass
-Q, K, V, dO, dQ), lse/D vectors left out.  A materialised score matrix would grow 16x from the
+each kernel must read and write once (forward Q, K, V, O; dK/dV pass Q, K, V, dO, dK, dV; dQ pass,
+which forms D = dO . O itself, Q, K, V, dO, O, dQ), lse/D vectors left out.  A materialised score matrix would grow 16x from the
 first row to the last; the ratio staying flat is the linear traffic of the tiled method
 ("FlashAttention and online softmax", "HBM traffic").  At N = 16384 (B = 1) one head's K and V
 (8 MB together) alone exceed an XCD's 4 MB L2, and the re-reads show up as the 1.4-1.5x ratio.  Source hashes
@@ -164,7 +164,7 @@ def sweep(dirpath: str, f_scale: float, w_scale: float) -> str:
     rows = ["| kernel | N | B | HBM MB | algorithmic MB | ratio |", "|---|---|---|---|---|---|"]
     d, H, e = 128, 16, 2
     for frag, label, tensors in (("fwd_bf16_kernel", "forward", 4), ("bwd_bf16_kernel", "dK/dV pass", 6),
-                                 ("bwd_dq_bf16_kernel", "dQ pass", 5)):
+                                 ("bwd_dq_bf16_kernel", "dQ pass", 6)):
         names = [n for n in fetch if frag in n and ("dq" in frag) == ("dq" in n)]
         if not names:
             continue

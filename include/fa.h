@@ -101,8 +101,8 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
                  void* workspace, size_t workspace_bytes, int B, int H, int N, int d,
                  float softmax_scale, int causal, int dtype, void* stream);
 
-/* The three stages fa_bwd runs, in this order, on one stream; a caller may run
- * them separately (e.g. to time or overlap them).  Same argument rules and codes as
+/* The three stages of the backward, to be run in this order on one stream; a caller
+ * may run them separately (e.g. to time or overlap them).  Same argument rules and codes as
  * fa_bwd for the pointers each stage takes.
  *   fa_bwd_preprocess : D_i = dO_i . O_i (the row term of dS = P o (dP - D),
  *                       "Backward pass: recompute instead of store", step 3) and
@@ -117,7 +117,10 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o,
  *                       P, dP and dS for every visible key tile and accumulates
  *                       dQ = scale dS K on chip (no atomics).  FA_DTYPE_FP32:
  *                       dQ = scale * accumulator.
- * fa_bwd_main and fa_bwd_dq read the workspace written by fa_bwd_preprocess. */
+ * fa_bwd_main and fa_bwd_dq read the workspace written by fa_bwd_preprocess.
+ *
+ * For FA_DTYPE_BF16, fa_bwd itself runs two launches: fa_bwd_dq_pre (below), then
+ * fa_bwd_main.  The results equal those of the three stages bit for bit. */
 fa_status fa_bwd_preprocess(const void* o, const void* dout, const float* lse,
                             void* workspace, size_t workspace_bytes, int B, int H,
                             int N, int d, int dtype, void* stream);
@@ -129,6 +132,15 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* dou
                     void* dq, void* workspace, size_t workspace_bytes, int B, int H,
                     int N, int d, float softmax_scale, int causal, int dtype,
                     void* stream);
+/* fa_bwd_preprocess and fa_bwd_dq in one pass (FA_DTYPE_BF16 only; FA_ERR_UNSUPPORTED
+ * for FA_DTYPE_FP32, whose dQ comes from fa_bwd_main's accumulator): each query row's
+ * D_i = dO_i . O_i and lse_i * log2(e) are formed where the dQ pass loads that row,
+ * used there, and written to the workspace for fa_bwd_main to run next.  Arguments as
+ * fa_bwd's (o and lse read, dq written). */
+fa_status fa_bwd_dq_pre(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* workspace,
+                        size_t workspace_bytes, int B, int H, int N, int d,
+                        float softmax_scale, int causal, int dtype, void* stream);
 
 /* ---- Variable-length batches and sliding windows ---------------------------------
  * fa_fwd_ex / fa_bwd_ex take the arguments of fa_fwd / fa_bwd plus:
@@ -160,6 +172,20 @@ fa_status fa_bwd_ex(const void* q, const void* k, const void* v, const void* o,
                     void* workspace, size_t workspace_bytes, const int* cu_seqlens, int B,
                     int H, int N, int total, int d, float softmax_scale, int causal,
                     int window, int dtype, void* stream);
+
+/* fa_bwd_ex's kernel launches one at a time (for timing them apart, or overlapping
+ * them with other work): `launches` is a mask of the launches to enqueue, in fa_bwd's
+ * order -- bf16: bit 0 fa_bwd_dq_pre's pass (dQ, and D and lse*log2(e) into the
+ * workspace), bit 1 the dK/dV pass; fp32: bit 0 preprocess, bit 1 dK/dV pass (which
+ * adds to the dQ accumulator), bit 2 dQ conversion.  Running the bits of
+ * FA_BWD_ALL_LAUNCHES in increasing order on one stream equals fa_bwd_ex.  Other
+ * arguments and errors as fa_bwd_ex; FA_ERR_INVALID_ARG for a mask outside 1..7. */
+#define FA_BWD_ALL_LAUNCHES 7
+fa_status fa_bwd_ex_launches(const void* q, const void* k, const void* v, const void* o,
+                             const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                             void* workspace, size_t workspace_bytes, const int* cu_seqlens,
+                             int B, int H, int N, int total, int d, float softmax_scale,
+                             int causal, int window, int dtype, int launches, void* stream);
 
 /* ---- Split-KV decoding ----------------------------------------------------------
  * "FlashAttention and online softmax" (Lesson 4), section "Split-KV for decoding

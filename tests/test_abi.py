@@ -112,3 +112,10 @@ def test_noalloc_size_limit_is_checked_on_the_host():
     assert L.fa_bwd_noalloc(None, *args(1, 1, 64, 64, 0)[1:]) == fa.FA_ERR_INVALID_ARG
     assert L.fa_bwd_noalloc(*args(1, 1, 64, 96, 0)) == fa.FA_ERR_UNSUPPORTED
     assert L.fa_status_string(fa.FA_ERR_TOO_LARGE) != b"unknown status"
+
+
+def test_bwd_ex_launches_mask_checked_on_the_host():
+    L = fa.lib()
+    for mask in (0, 8, -1):
+        assert L.fa_bwd_ex_launches(P, P, P, P, P, P, P, P, P, P, 1 << 30, None, 1, 2, 100, 0, 64, 0.125,
+                                    1, 0, 0, mask, None) == fa.FA_ERR_INVALID_ARG

@@ -239,22 +239,31 @@ def test_memory_stays_linear_long_context(dev):
     assert peak < (8 << 30) // 8
 
 
-def test_bwd_stages_equal_fa_bwd(dev):
-    """fa_bwd_preprocess + fa_bwd_main + fa_bwd_dq reproduce fa_bwd."""
-    w = Workload("stages", 1, 3, 500, 128, True, "bf16", True, seed=7)
-    say("[stages] bwd in three calls vs one")
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_stages_equal_fa_bwd(dev, dtype, d):
+    """fa_bwd_preprocess + fa_bwd_main + fa_bwd_dq, and fa_bwd's own launches
+    (bf16: fa_bwd_dq_pre with the preprocess folded in, then fa_bwd_main), reproduce
+    fa_bwd bit for bit (fp32 dQ: up to its atomics' summation order)."""
+    w = Workload("stages", 1, 3, 500, d, True, dtype, True, seed=7)
+    say(f"[stages] bwd in separate calls vs one, {dtype} d={d}")
     x = make_inputs(w)
     q, k, v, o, lse = gpu_fwd(x, w, dev)
     do = x["do"].to(dev)
     dq1, dk1, dv1 = fa.bwd(q, k, v, o, do, lse, w.scale, True)
-    ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
-    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
-    for stage in fa.bwd_stages(q, k, v, o, do, lse, w.scale, True, ws, grads):
-        stage()
-    torch.cuda.synchronize()
-    dq2, dk2, dv2 = grads
-    assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2)
-    check_grad("bf16", dq2, f64(dq1), "dQ", "stages")
+    for fused in (False, True):
+        ws = torch.full((fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype),), 0xFF, dtype=torch.uint8,
+                        device=dev)
+        grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+        for stage in fa.bwd_stages(q, k, v, o, do, lse, w.scale, True, ws, grads, fused=fused):
+            stage()
+        torch.cuda.synchronize()
+        dq2, dk2, dv2 = grads
+        assert torch.equal(dk1, dk2) and torch.equal(dv1, dv2), f"fused={fused}"
+        if dtype == "bf16":
+            assert torch.equal(dq1, dq2), f"fused={fused}"
+        else:
+            check_grad("fp32", dq2, f64(dq1), "dQ", "stages")
 
 
 def test_calls_run_on_the_current_stream(dev):

@@ -14,7 +14,7 @@ from exact_io_aware_14_amd.inputs import (VARLEN_WORKLOADS, WINDOW_WORKLOADS, Va
                                           Workload, make_inputs, make_varlen_inputs, to_f64)
 from oracle import attention_bwd, attention_fwd
 from oracle.varlen import varlen_bwd, varlen_fwd, window_mask
-from parity import check_fwd, check_grad
+from parity import check_fwd, check_grad, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -194,3 +194,32 @@ def test_binding_checks_cu_seqlens(dev):
     with pytest.raises(ValueError):
         fa.bwd_ex(qp, qp, qp, o, do, lse, None, True, cu_seqlens=cu_dev([0, 50, 64]), max_seqlen=49)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_bwd_ex_launches_one_by_one(dev, dtype):
+    """fa_bwd_ex_launches: the backward's launches enqueued one at a time, in order,
+    equal fa_bwd_ex (bf16 bit for bit; fp32 dQ up to its atomics' order)."""
+    lens = [37, 0, 200, 64]
+    w = VarlenWorkload("launches", len(lens), 1, 1, 3, 64, True, dtype, seed=11)
+    x = make_varlen_inputs(w, lengths=lens)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    args = dict(scale=w.scale, causal=True, window=50, cu_seqlens=x["cu"].to(dev), max_seqlen=x["max_len"])
+    o, lse = fa.fwd_ex(q, k, v, **args)
+    ref = fa.bwd_ex(q, k, v, o, do, lse, **args)
+    ws = torch.full((fa.workspace_bytes(len(lens), 3, x["max_len"], 64, q.dtype),), 0xFF, dtype=torch.uint8,
+                    device=dev)
+    grads = tuple(torch.full_like(q, float("nan")) for _ in range(3))
+    masks = (1, 2) if dtype == "bf16" else (1, 2, 4)
+    for m in masks:
+        fa.bwd_ex(q, k, v, o, do, lse, workspace=ws, grads=grads, launches=m, **args)
+    torch.cuda.synchronize()
+    assert torch.equal(grads[1], ref[1]) and torch.equal(grads[2], ref[2])
+    if dtype == "bf16":
+        assert torch.equal(grads[0], ref[0])
+    else:
+        check_grad("fp32", grads[0], f64(ref[0]), "dQ", "launches")
+    for bad in (0, 8):
+        with pytest.raises(fa.FaError) as e:
+            fa.bwd_ex(q, k, v, o, do, lse, workspace=ws, grads=grads, launches=bad, **args)
+        assert e.value.status == fa.FA_ERR_INVALID_ARG
