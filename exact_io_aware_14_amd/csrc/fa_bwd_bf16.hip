@@ -88,14 +88,20 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
 
   // Four sets of Q, dO, lse and D tile buffers, each named statically in the (four
   // times unrolled) step loop: tile t+2 lands while tiles t-1, t and t+1 are read.
-  __shared__ __attribute__((aligned(1024))) __bf16 Q0[C::QTILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Q1[C::QTILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Q2[C::QTILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 Q3[C::QTILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 G0[C::QTILE];  // dO
-  __shared__ __attribute__((aligned(1024))) __bf16 G1[C::QTILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 G2[C::QTILE];
-  __shared__ __attribute__((aligned(1024))) __bf16 G3[C::QTILE];
+  // Each set holds its Q tile followed by its dO tile, so one address reaches a row of
+  // both (the dO read adds a fixed instruction offset).
+  __shared__ __attribute__((aligned(1024))) __bf16 S0[2 * C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 S1[2 * C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 S2[2 * C::QTILE];
+  __shared__ __attribute__((aligned(1024))) __bf16 S3[2 * C::QTILE];
+  __bf16* const Q0 = S0;
+  __bf16* const Q1 = S1;
+  __bf16* const Q2 = S2;
+  __bf16* const Q3 = S3;
+  __bf16* const G0 = S0 + C::QTILE;  // dO
+  __bf16* const G1 = S1 + C::QTILE;
+  __bf16* const G2 = S2 + C::QTILE;
+  __bf16* const G3 = S3 + C::QTILE;
   __shared__ __attribute__((aligned(16))) float L0[C::BQ];
   __shared__ __attribute__((aligned(16))) float L1[C::BQ];
   __shared__ __attribute__((aligned(16))) float L2s[C::BQ];
@@ -232,8 +238,8 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   // barrier, and these reads run under the previous step's dV/dK products.
   bf16x8_t aq[NKK], ag[NKK];
   auto prefetch_rows = [&](const __bf16* Qb, const __bf16* Gb, int kk) {
-    lds_read_a(aq[kk], Qb + nat[kk]);
-    lds_read_a(ag[kk], Gb + nat[kk]);
+    (void)Gb;  // == Qb + QTILE
+    lds_read_a_pair<C::QTILE * 2>(aq[kk], ag[kk], Qb + nat[kk]);
   };
 
   // Step qt (tile t in buffer set (t - qt0) % 4; p = tile qt-1, c = tile qt, n = tile

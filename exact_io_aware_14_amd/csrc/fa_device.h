@@ -112,13 +112,19 @@ __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; 
 // kernel, so LDS reads can no longer run ahead of the matrix products that consume
 // them.  The compiler therefore does not track these loads: every caller waits for
 // them itself (s_waitcnt vmcnt(0), then a barrier) before the tile is read.
+// LDS byte address of a pointer into a __shared__ array.  A generic pointer to LDS
+// carries the LDS offset in its low 32 bits (the high bits are the shared aperture),
+// so truncation gives it without the null test an address-space cast emits.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(unsigned long long)p;
+}
+
 __device__ __forceinline__ void dma16(const void* base, unsigned voff, const void* lds_wave) {
   const unsigned long long t = (unsigned long long)base;
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)t);
   const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(t >> 32));
   const unsigned long long sbase = ((unsigned long long)hi << 32) | lo;
-  const unsigned m0 = __builtin_amdgcn_readfirstlane(
-      (unsigned)(unsigned long long)(const __attribute__((address_space(3))) void*)lds_wave);
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave));
   // M0 (the LDS destination) is bound as an operand, so the compiler sets it itself.
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
@@ -214,8 +220,15 @@ __device__ __forceinline__ void mma_v_aa(f32x16_t& acc, const bf16x8_t& a, const
 // instruction reads dst, and keeps it in order with the products that consume dst
 // by issuing those as inline assembly too.
 __device__ __forceinline__ void lds_read_a(bf16x8_t& dst, const __bf16* p) {
-  const unsigned addr = (unsigned)(unsigned long long)(const __attribute__((address_space(3))) void*)p;
+  const unsigned addr = lds_addr(p);
   asm volatile("ds_read_b128 %0, %1" : "=a"(dst) : "v"(addr) : "memory");
+}
+// Two 16-byte LDS reads into AGPRs from one address: p and p + OFF bytes (OFF an
+// instruction offset).  Same waiting rules as lds_read_a.
+template <int OFF>
+__device__ __forceinline__ void lds_read_a_pair(bf16x8_t& d0, bf16x8_t& d1, const __bf16* p) {
+  const unsigned addr = lds_addr(p);
+  asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:%3" : "=&a"(d0), "=a"(d1) : "v"(addr), "i"(OFF) : "memory");
 }
 // MFMA results in VGPRs may now be touched by vector code.
 __device__ __forceinline__ void mfma_v_ready(f32x16_t& x, f32x16_t& y) {
