@@ -3,17 +3,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step = one forward (fa_fwd) and one backward (fa_bwd: preprocess, main = dK
-and dV, dq) over the workload's batch, inputs resident in HBM.  Default workload:
-the long causal layer B=4, H=32, N=4096, d=128, bf16 (planted query row), with
-dO as the fourth seeded draw.  FLOPs credited: forward 4*B*H*N^2*d halved for
-causal, backward 2.5x that.
+One step = one forward (fa_fwd) and one backward (fa_bwd: for bf16 the dQ pass with
+the preprocess folded in, then the dK/dV pass) over the workload's batch, inputs
+resident in HBM.  Default workload: the long causal layer B=4, H=32, N=4096,
+d=128, bf16 (planted query row), with dO as the fourth seeded draw.  FLOPs
+credited: forward 4*B*H*N^2*d halved for causal, backward 2.5x that.
 
 Prints one JSON line.  ``value`` is forward+backward TFLOP/s over the timed
 steps (wall clock between device synchronisations).  ``roofline`` covers the
 kernel with the largest average duration, timed with HIP events on the stream it
-runs on; its FLOPs are the matrix products that kernel performs (forward: 2 per
-score, dK/dV pass: 4, dQ pass: 3; each 2*d FLOPs per visible score).
+runs on; its FLOPs are the method's matrix products that kernel performs
+(forward: 2 per visible score; dK/dV pass: 4; dQ pass: 1, its dQ product -- its
+two recomputed products are not credited), each 2*d FLOPs.  ``clock`` is the
+shader clock and board power sampled while the same step runs back to back for
+1.5 s after the timed steps.  ``configs``
+gives every workload's rates against both peak figures (2500 and 2516.6 TFLOP/s).
 ``cpu_baseline`` times the CPU fp64 oracle on a bounded sample of the same
 workload (whole heads).
 """
@@ -31,6 +35,7 @@ if ROOT not in sys.path:
 
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, N=4096 d=128) + % MFMA peak"
 PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+PEAK_ALT = 2516.6     # the same peak as 256 CUs x 4 SIMDs x 1024 FLOP/clk x 2.4 GHz
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -180,6 +185,70 @@ def _timed(calls, steps: int, warmup: int):
     return [sum(e[i].elapsed_time(e[i + 1]) for e in evs) / steps for i in range(len(calls))]
 
 
+KERNEL_NAMES = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel", "bwd_dq_pre": "bwd_dq_kernel",
+                "bwd_dq": "bwd_dq_kernel", "bwd_preprocess": "bwd_pre_kernel"}
+
+
+def _roofline(kernels: dict, workload: str) -> dict:
+    """MFMA roofline of the longest kernel: kernels = {name: (ms, credited FLOPs)}."""
+    dom = max(kernels, key=lambda n: kernels[n][0])
+    ms, flops = kernels[dom]
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 2), "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(KERNEL_NAMES[dom], workload)}
+
+
+def _pct(tflops: float) -> dict:
+    return {"tflops": round(tflops, 1), "pct_of_2500": round(100 * tflops / PEAK_TFLOPS, 2),
+            "pct_of_2516.6": round(100 * tflops / PEAK_ALT, 2)}
+
+
+def configs_measure(dev, steps: int, warmup: int, headline_name: str, headline: dict) -> dict:
+    """Every workload of the input recipe at full size: forward (and backward where the
+    workload has one) time, TFLOP/s against both peak figures, and the clock sampled
+    while it ran.  The headline layer's line comes from the main measurement."""
+    import torch
+
+    from exact_io_aware_14_amd import fa
+    from exact_io_aware_14_amd.accounting import bwd_flops, fwd_flops
+    from exact_io_aware_14_amd.inputs import WORKLOADS, make_inputs
+    from exact_io_aware_14_amd.telemetry import soak
+
+    out = {}
+    for name, w in WORKLOADS.items():
+        if name == headline_name:
+            out[name] = headline
+            continue
+        if w.dtype != "bf16":  # the fp32 tiny case is a parity case, not a rate
+            continue
+        x = make_inputs(w, with_do=True)
+        q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+        o, lse = fa.fwd(q, k, v, w.scale, w.causal)
+        ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
+        grads = tuple(torch.empty_like(q) for _ in range(3))
+        calls = [lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)]
+        if w.backward:
+            calls.append(lambda: fa.bwd(q, k, v, o, do, lse, w.scale, w.causal, workspace=ws, grads=grads))
+        times = _timed(calls, steps, warmup)
+
+        def one_step():
+            for c in calls:
+                c()
+        clock = soak(one_step, 1.0, torch.cuda.synchronize)
+        ff, bf = fwd_flops(w.B, w.H, w.N, w.d, w.causal), bwd_flops(w.B, w.H, w.N, w.d, w.causal)
+        rec = {"workload": {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
+               "fwd_ms": round(times[0], 4), "fwd": _pct(ff / times[0] / 1e9)}
+        if w.backward:
+            rec["bwd_ms"] = round(times[1], 4)
+            rec["bwd"] = _pct(bf / times[1] / 1e9)
+            rec["fwd_bwd"] = _pct((ff + bf) / (times[0] + times[1]) / 1e9)
+        rec["clock"] = clock
+        out[name] = rec
+        del x, q, k, v, do, o, lse, ws, grads
+    return out
+
+
 def ex_measure(dev, steps: int, warmup: int, cpu: bool):
     """Sliding window (window_long) and variable-length batch (varlen_mix): fwd and bwd
     time, credited TFLOP/s over the visible pairs, and the same data without the
@@ -200,9 +269,13 @@ def ex_measure(dev, steps: int, warmup: int, cpu: bool):
     o, lse = fa.fwd_ex(q, k, v, w.scale, True, W)
     ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
     grads = tuple(torch.empty_like(q) for _ in range(3))
-    t_f, t_b = _timed([lambda: fa.fwd_ex(q, k, v, w.scale, True, W, out=o, lse=lse),
-                       lambda: fa.bwd_ex(q, k, v, o, do, lse, w.scale, True, W, workspace=ws, grads=grads)],
-                      steps, warmup)
+    t_f, t_dq, t_main = _timed([lambda: fa.fwd_ex(q, k, v, w.scale, True, W, out=o, lse=lse),
+                                lambda: fa.bwd_ex(q, k, v, o, do, lse, w.scale, True, W, workspace=ws,
+                                                  grads=grads, launches=1),
+                                lambda: fa.bwd_ex(q, k, v, o, do, lse, w.scale, True, W, workspace=ws,
+                                                  grads=grads, launches=2)],
+                               steps, warmup)
+    t_b = t_dq + t_main
     o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
     c_f, c_b = _timed([lambda: fa.fwd(q, k, v, w.scale, True, out=o2, lse=lse2),
                        lambda: fa.bwd(q, k, v, o2, do, lse2, w.scale, True, workspace=ws, grads=grads)],
@@ -215,9 +288,9 @@ def ex_measure(dev, steps: int, warmup: int, cpu: bool):
            "causal_without_window_ms": {"fwd": round(c_f, 4), "bwd": round(c_b, 4)},
            "speedup_vs_causal": round((c_f + c_b) / (t_f + t_b), 3),
            "visible_pair_ratio": round(window_pairs(w.N, 0) / window_pairs(w.N, W), 3),
-           "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(ff / t_f / 1e9, 1),
-                        "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ff / t_f / 1e9 / PEAK_TFLOPS, 4),
-                        "traffic": None}}
+           "kernel_ms": {"fwd": round(t_f, 4), "bwd_dq_pre": round(t_dq, 4), "bwd_main": round(t_main, 4)},
+           "roofline": _roofline({"fwd": (t_f, ff), "bwd_dq_pre": (t_dq, 0.5 * ff), "bwd_main": (t_main, 2.0 * ff)},
+                                 w.name)}
     if cpu:
         from oracle import attention_bwd, attention_fwd
         from oracle.varlen import window_mask
@@ -243,10 +316,12 @@ def ex_measure(dev, steps: int, warmup: int, cpu: bool):
     o, lse = fa.fwd_ex(q, k, v, vw.scale, vw.causal, cu_seqlens=cu, max_seqlen=nmax)
     ws = torch.empty(fa.workspace_bytes(len(lens), vw.H, nmax, vw.d, q.dtype), dtype=torch.uint8, device=dev)
     grads = tuple(torch.empty_like(q) for _ in range(3))
-    t_f, t_b = _timed([lambda: fa.fwd_ex(q, k, v, vw.scale, vw.causal, cu_seqlens=cu, max_seqlen=nmax,
-                                         out=o, lse=lse),
-                       lambda: fa.bwd_ex(q, k, v, o, do, lse, vw.scale, vw.causal, cu_seqlens=cu,
-                                         max_seqlen=nmax, workspace=ws, grads=grads)], steps, warmup)
+    bx = lambda m: fa.bwd_ex(q, k, v, o, do, lse, vw.scale, vw.causal, cu_seqlens=cu, max_seqlen=nmax,
+                             workspace=ws, grads=grads, validate=False, launches=m)
+    t_f, t_dq, t_main = _timed([lambda: fa.fwd_ex(q, k, v, vw.scale, vw.causal, cu_seqlens=cu,
+                                                  max_seqlen=nmax, out=o, lse=lse, validate=False),
+                                lambda: bx(1), lambda: bx(2)], steps, warmup)
+    t_b = t_dq + t_main
     # the same sequences zero-padded to the longest one, as a dense [B, H, max, d] batch
     B = len(lens)
     pad = lambda t: torch.zeros((B, vw.H, nmax, vw.d), dtype=t.dtype, device=dev)
@@ -269,9 +344,9 @@ def ex_measure(dev, steps: int, warmup: int, cpu: bool):
            "fwd_tflops": round(ff / t_f / 1e9, 1), "bwd_tflops": round(2.5 * ff / t_b / 1e9, 1),
            "padded_dense_ms": {"fwd": round(p_f, 4), "bwd": round(p_b, 4)},
            "speedup_vs_padded": round((p_f + p_b) / (t_f + t_b), 3),
-           "roofline": {"bound": "mfma", "kernel": "fwd_kernel", "achieved": round(ff / t_f / 1e9, 1),
-                        "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(ff / t_f / 1e9 / PEAK_TFLOPS, 4),
-                        "traffic": None}}
+           "kernel_ms": {"fwd": round(t_f, 4), "bwd_dq_pre": round(t_dq, 4), "bwd_main": round(t_main, 4)},
+           "roofline": _roofline({"fwd": (t_f, ff), "bwd_dq_pre": (t_dq, 0.5 * ff), "bwd_main": (t_main, 2.0 * ff)},
+                                 vw.name)}
     if cpu:
         from oracle.varlen import varlen_fwd
 
@@ -333,6 +408,46 @@ def secondary_measure(dev, steps: int, warmup: int):
     return out
 
 
+def traffic_run_ex(dev, name: str) -> int:
+    """For rocprofv3 counter passes on the windowed or variable-length workload: the
+    calibration copy, then its forward and backward twice (warm-up, counted)."""
+    import torch
+
+    from exact_io_aware_14_amd import fa
+    from exact_io_aware_14_amd.inputs import (VARLEN_WORKLOADS, WINDOW_WORKLOADS, make_inputs,
+                                              make_varlen_inputs)
+    from exact_io_aware_14_amd.traffic import COPY_BYTES
+
+    if name in WINDOW_WORKLOADS:
+        w, W = WINDOW_WORKLOADS[name]
+        x = make_inputs(w)
+        q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+        args = dict(scale=w.scale, causal=True, window=W)
+    elif name in VARLEN_WORKLOADS:
+        vw = VARLEN_WORKLOADS[name]
+        xv = make_varlen_inputs(vw)
+        q, k, v, do = (xv[n].to(dev) for n in ("q", "k", "v", "do"))
+        args = dict(scale=vw.scale, causal=vw.causal, cu_seqlens=xv["cu"].to(dev), max_seqlen=xv["max_len"])
+    else:
+        print(f"unknown workload {name}", file=sys.stderr)
+        return 2
+
+    def run():
+        o, lse = fa.fwd_ex(q, k, v, **args)
+        fa.bwd_ex(q, k, v, o, do, lse, **args)
+
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    run()
+    torch.cuda.synchronize()
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    run()
+    torch.cuda.synchronize()
+    print(json.dumps({"traffic_run": name, "copy_bytes": COPY_BYTES}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,6 +478,8 @@ def main(argv=None) -> int:
         return 1
     fa.lib()
     dev = torch.device("cuda:0")
+    if args.traffic_run and args.workload not in WORKLOADS:
+        return traffic_run_ex(dev, args.workload)
     w = WORKLOADS[args.workload]
     x = make_inputs(w, with_do=True)
     q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
@@ -370,8 +487,9 @@ def main(argv=None) -> int:
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     grads = tuple(torch.empty_like(q) for _ in range(3))
     ws = torch.empty(fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype), dtype=torch.uint8, device=dev)
-    stages = fa.bwd_stages(q, k, v, o, do, lse, w.scale, w.causal, ws, grads)
-    names = ["fwd", "bwd_preprocess", "bwd_main", "bwd_dq"]
+    stages = fa.bwd_stages(q, k, v, o, do, lse, w.scale, w.causal, ws, grads, fused=True)
+    names = ["fwd"] + (["bwd_dq_pre", "bwd_main"] if len(stages) == 2 else
+                       ["bwd_preprocess", "bwd_main", "bwd_dq"])
     calls = [lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)] + stages
 
     def step(evs=None):
@@ -412,6 +530,8 @@ def main(argv=None) -> int:
         print(json.dumps({"traffic_run": w.name, "copy_bytes": COPY_BYTES}), flush=True)
         return 0
 
+    from exact_io_aware_14_amd.telemetry import soak
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -421,6 +541,8 @@ def main(argv=None) -> int:
         step(evs[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    # the clock and power of the same step held for ~1.5 s (the metrics refresh ~1/s)
+    clock = soak(step, 1.5, torch.cuda.synchronize)
     ms_step = (t1 - t0) * 1e3 / args.steps
     per = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps for i, n in enumerate(names)}
     samples = {n: sorted(e[i].elapsed_time(e[i + 1]) for e in evs) for i, n in enumerate(names)}
@@ -429,16 +551,16 @@ def main(argv=None) -> int:
 
     ff = fwd_flops(w.B, w.H, w.N, w.d, w.causal)
     bf = bwd_flops(w.B, w.H, w.N, w.d, w.causal)
-    bwd_ms = per["bwd_preprocess"] + per["bwd_main"] + per["bwd_dq"]
+    bwd_ms = sum(per[n] for n in names[1:])
     value = (ff + bf) / (ms_step * 1e-3) / 1e12
     fwd_t = ff / (per["fwd"] * 1e-3) / 1e12
     bwd_t = bf / (bwd_ms * 1e-3) / 1e12
-    # algorithmic FLOPs each kernel performs: 2*d per visible score per product
-    kflops = {"fwd": ff, "bwd_main": 2.0 * ff, "bwd_dq": 1.5 * ff}
-    kernel_names = {"fwd": "fwd_kernel", "bwd_main": "bwd_main_kernel", "bwd_dq": "bwd_dq_kernel"}
-    dom = max(kflops, key=lambda n: per[n])
-    achieved = kflops[dom] / (per[dom] * 1e-3) / 1e12
-    traffic = measured_traffic(kernel_names[dom], w.name)
+    # the method's products each kernel performs (2*d FLOPs per visible score each):
+    # forward 2, dK/dV pass 4, dQ pass 1 (its recomputed S and dP are not credited)
+    kflops = {"fwd": ff, "bwd_main": 2.0 * ff, "bwd_dq_pre": 0.5 * ff, "bwd_dq": 0.5 * ff, "bwd_preprocess": 0.0}
+    roof = _roofline({n: (per[n], kflops[n]) for n in names}, w.name)
+    # executed matrix FLOPs (dQ pass: 3 products), for comparison with the MFMA counters
+    xflops = {"fwd": ff, "bwd_main": 2.0 * ff, "bwd_dq_pre": 1.5 * ff, "bwd_dq": 1.5 * ff, "bwd_preprocess": 0.0}
 
     props = torch.cuda.get_device_properties(dev)
     rec = {
@@ -462,14 +584,20 @@ def main(argv=None) -> int:
         "bwd_tflops": round(bwd_t, 2),
         "bwd_pct_peak": round(100 * bwd_t / PEAK_TFLOPS, 2),
         "fwd_bwd_pct_peak": round(100 * value / PEAK_TFLOPS, 2),
+        "pct_of_2516.6": {"fwd": round(100 * fwd_t / PEAK_ALT, 2), "bwd": round(100 * bwd_t / PEAK_ALT, 2),
+                          "fwd_bwd": round(100 * value / PEAK_ALT, 2)},
         "kernel_ms": {n: round(m, 4) for n, m in per.items()},
         "kernel_ms_median": {n: round(m, 4) for n, m in med.items()},
         "kernel_ms_min": {n: round(v[0], 4) for n, v in samples.items()},
-        "roofline": {"bound": "mfma", "kernel": kernel_names[dom], "achieved": round(achieved, 2),
-                     "peak": PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS, 4),
-                     "traffic": traffic},
+        "kernel_executed_tflops": {n: round(xflops[n] / (per[n] * 1e-3) / 1e12, 1) for n in names},
+        "roofline": roof,
+        "clock": clock,
         "device": props.name,
     }
+    headline = {"workload": {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal},
+                "fwd_ms": round(per["fwd"], 4), "fwd": _pct(fwd_t), "bwd_ms": round(bwd_ms, 4),
+                "bwd": _pct(bwd_t), "fwd_bwd": _pct((ff + bf) / ((per["fwd"] + bwd_ms) * 1e-3) / 1e12),
+                "clock": rec["clock"]}
     if args.cpu_heads > 0:
         heads = [(i // w.H, i % w.H) for i in range(min(args.cpu_heads, w.B * w.H))]
         cb, par = cpu_baseline(x, w, heads, (o, lse) + grads)
@@ -481,6 +609,7 @@ def main(argv=None) -> int:
         rec["next_rows"] = {"splitkv_decode": decode_measure(dev, args.steps, args.warmup, args.cpu_heads > 0)}
         rec["next_rows"].update(ex_measure(dev, min(args.steps, 10), min(args.warmup, 3), args.cpu_heads > 0))
         rec["secondary"] = secondary_measure(dev, min(args.steps, 10), min(args.warmup, 3))
+        rec["configs"] = configs_measure(dev, min(args.steps, 10), min(args.warmup, 3), w.name, headline)
     print(json.dumps(rec), flush=True)
     return 0
 
