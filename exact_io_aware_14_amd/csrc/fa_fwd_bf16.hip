@@ -34,6 +34,10 @@ namespace fa {
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
+// Bound on a lane's sum of weights in one tile before the reference must move (see the
+// softmax in the tile loop); far inside fp32 and bf16 range.
+constexpr float kWeightBound = 1048576.0f;  // 2^20
+
 template <int D>
 struct FwdFast {
   static constexpr int NW = 4;             // waves per workgroup
@@ -169,6 +173,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) oacc[dt] = zero16();
   float mref = kNoMax, lsum = 0.0f, lsum_bf = 0.0f;
+  bool first = true;  // no reference yet: the first tile a wave computes takes the max
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
   const bf16x2_t ones2 = {(__bf16)1.0f, (__bf16)1.0f};
   const float c = scale * kLog2e;
@@ -184,81 +189,111 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     const int k0 = kt * C::BC;
     if (causal && k0 > qw + 31) return;  // tile wholly above this wave's rows
     if (window > 0 && k0 + C::BC - 1 <= qw - window) return;  // wholly below their band
-    // S^T = K Q^T
+    // S^T = K Q^T (a lambda: the rare path below computes it a second time)
     constexpr int NKS = C::NKS;
     // K operand reads run AHEAD d-steps in front of the products that use them, so
     // the LDS round trips overlap each other and the products instead of alternating
     // with them (at most 15 LDS reads may be outstanding for a counted wait).
     constexpr int AHEAD = NKK < 4 ? NKK : 4;
-    f32x16_t s[NKS];
-    bf16x8_t ka[NKK][NKS];
-    auto read_k = [&](int kk) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        ka[kk][ks] = *reinterpret_cast<const bf16x8_t*>(
-            Kb + k_rd + (ks * 2 * CPR * 16 + kk * 2 * 16) * 8);
-    };
-    // Wave priority 1 while the wave issues its products, 0 during its softmax: when
-    // both waves of a SIMD are ready, the one feeding the matrix cores goes first, and
-    // the other's vector work fills in, which pushes the two into opposite phases.  (The
-    // general variant measured slightly slower with it and keeps a flat priority.)
-    if constexpr (!GEN) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kk = 0; kk < AHEAD; ++kk) read_k(kk);
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) s[ks] = zero16();
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk + AHEAD < NKK) read_k(kk + AHEAD);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-        s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][ks], qop[kk], s[ks], 0, 0, 0);
-    }
-
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (!GEN) __builtin_amdgcn_s_setprio(0);
     const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw) ||
                            (window > 0 && k0 <= qw + 31 - window);
-    if (need_mask) {  // keys past the end, above the diagonal or below the window
-      const int hi = causal ? min(myq, N - 1) : N - 1;
-      const int lo = window > 0 ? myq - window + 1 : 0;
+    f32x16_t s[NKS];
+    auto scores = [&]() {
+      bf16x8_t ka[NKK][NKS];
+      auto read_k = [&](int kk) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) mask_rows<GEN>(s[ks], g, k0 + ks * 32, lo, hi);
-    }
-
-    // Online softmax: tile max, lazily moved reference, p = 2^(s*c - mref*c).
-    float mx = s[0][0];
+        for (int ks = 0; ks < NKS; ++ks)
+          ka[kk][ks] = *reinterpret_cast<const bf16x8_t*>(
+              Kb + k_rd + (ks * 2 * CPR * 16 + kk * 2 * 16) * 8);
+      };
+      // Wave priority 1 while the wave issues its products, 0 during its softmax: when
+      // both waves of a SIMD are ready, the one feeding the matrix cores goes first, and
+      // the other's vector work fills in, which pushes the two into opposite phases.  (The
+      // general variant measured slightly slower with it and keeps a flat priority.)
+      if constexpr (!GEN) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+      for (int kk = 0; kk < AHEAD; ++kk) read_k(kk);
 #pragma unroll
-    for (int ks = 1; ks < NKS; ++ks)
+      for (int ks = 0; ks < NKS; ++ks) s[ks] = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
-    {  // the other half of the wave holds the other keys of the same query columns
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-    }
-    const bool move = mx > mref + grow;
-    if (__builtin_amdgcn_ballot_w64(move)) {  // wave-uniform: rare after the first tile
-      const float mnew = move ? mx : mref;
-      const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);
-      lsum *= alpha;
-      lsum_bf *= alpha;
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + AHEAD < NKK) read_k(kk + AHEAD);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
-      mref = mnew;
-    }
-    const float mc = mref * c;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
-        s[ks][r] = p;
-        lsum += p;
+        for (int ks = 0; ks < NKS; ++ks)
+          s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][ks], qop[kk], s[ks], 0, 0, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!GEN) __builtin_amdgcn_s_setprio(0);
+      if (need_mask) {  // keys past the end, above the diagonal or below the window
+        const int hi = causal ? min(myq, N - 1) : N - 1;
+        const int lo = window > 0 ? myq - window + 1 : 0;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) mask_rows<GEN>(s[ks], g, k0 + ks * 32, lo, hi);
+      }
+    };
+    scores();
+
+    // Online softmax against the lazily moved reference mref: p = 2^(s*c - mref*c).
+    // The theorem's exactness needs only one common reference for l and o~, and the
+    // reference only has to keep the weights bounded.  So after the first tile the
+    // weights are formed against the current reference straight away, and the tile's
+    // sum of weights per lane bounds every one of them: while no lane's sum exceeds
+    // 2^20 nothing needs to move.  Otherwise (a score beyond the reference by more than
+    // about 15 in the exp2 domain, or the first tile) the tile is redone: the scores
+    // again from the K tile still in LDS, their max, the move, and the weights.
+    // (d = 64 keeps a max every tile: the second copy of the scores code would cost it
+    // its third wave per SIMD, which it needs more.)
+    constexpr bool kSkipMax = D == 128;
+    float t = 0.0f;
+    if (kSkipMax && !first) {
+      const float mc = mref * c;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
+          s[ks][r] = p;
+          t += p;
+        }
+    }
+    if (!kSkipMax || first || __builtin_amdgcn_ballot_w64(!(t <= kWeightBound))) {  // wave-uniform, rare
+      if (kSkipMax && !first) scores();
+      first = false;
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+      for (int ks = 1; ks < NKS; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[ks][r]);
+      {  // the other half of the wave holds the other keys of the same query columns
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const bool move = mx > mref + grow;
+      if (__builtin_amdgcn_ballot_w64(move)) {
+        const float mnew = move ? mx : mref;
+        const float alpha = __builtin_amdgcn_exp2f((mref - mnew) * c);
+        lsum *= alpha;
+        lsum_bf *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) oacc[dt] *= alpha;
+        mref = mnew;
+      }
+      const float mc = mref * c;
+      t = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
+          s[ks][r] = p;
+          t += p;
+        }
+    }
+    lsum += t;
 
     // O^T += V^T P^T
     if constexpr (!GEN) __builtin_amdgcn_s_setprio(1);
