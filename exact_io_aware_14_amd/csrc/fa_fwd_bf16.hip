@@ -241,25 +241,32 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     // weights are formed against the current reference straight away, and the tile's
     // sum of weights per lane bounds every one of them: while no lane's sum exceeds
     // 2^20 nothing needs to move.  Otherwise (a score beyond the reference by more than
-    // about 15 in the exp2 domain, or the first tile) the tile is redone: the scores
-    // again from the K tile still in LDS, their max, the move, and the weights.
-    // (d = 64 keeps a max every tile: the second copy of the scores code would cost it
-    // its third wave per SIMD, which it needs more.)
-    constexpr bool kSkipMax = D == 128;
+    // about 15 in the exp2 domain, or the first tile) the scores' max moves the
+    // reference and the weights are formed again.  The scores for that come from
+    // registers of their own at d = 64; at d = 128, where those registers would cost
+    // more, the weights overwrite the scores and the rare path computes the scores
+    // again from the K tile still in LDS.
+    constexpr bool kKeepScores = D == 64;
+    f32x16_t pst[kKeepScores ? NKS : 1];
+    auto P = [&](int ks) -> f32x16_t& {
+      if constexpr (kKeepScores) return pst[ks];
+      else return s[ks];
+    };
     float t = 0.0f;
-    if (kSkipMax && !first) {
+    if (!first) {
       const float mc = mref * c;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
-          s[ks][r] = p;
-          t += p;
+          P(ks)[r] = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
+          t += P(ks)[r];
         }
     }
-    if (!kSkipMax || first || __builtin_amdgcn_ballot_w64(!(t <= kWeightBound))) {  // wave-uniform, rare
-      if (kSkipMax && !first) scores();
+    if (first || __builtin_amdgcn_ballot_w64(!(t <= kWeightBound))) {  // wave-uniform, rare
+      if constexpr (!kKeepScores) {
+        if (!first) scores();
+      }
       first = false;
       float mx = s[0][0];
 #pragma unroll
@@ -288,9 +295,8 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
-          s[ks][r] = p;
-          t += p;
+          P(ks)[r] = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
+          t += P(ks)[r];
         }
     }
     lsum += t;
@@ -303,7 +309,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
       for (int j = 0; j < 2; ++j) {
         bf16x8_t pb;
 #pragma unroll
-        for (int sl = 0; sl < 8; ++sl) pb[sl] = (__bf16)s[ks][j * 8 + sl];
+        for (int sl = 0; sl < 8; ++sl) pb[sl] = (__bf16)P(ks)[j * 8 + sl];
         lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 0, 1), ones2, lsum_bf, false);
         lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 2, 3), ones2, lsum_bf, false);
         lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 4, 5), ones2, lsum_bf, false);
