@@ -66,31 +66,33 @@ def cpu_baseline(x, w, heads, outs):
 
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     t = 0.0
-    worst = {"O": 0.0, "lse": 0.0, "dQ": 0.0, "dK": 0.0, "dV": 0.0}
-    o, lse, dq, dk, dv = (z.float().cpu().double().numpy() for z in outs)
+    backward = len(outs) == 5
+    worst = {"O": 0.0, "lse": 0.0} | ({"dQ": 0.0, "dK": 0.0, "dV": 0.0} if backward else {})
+    outs = [z.float().cpu().double().numpy() for z in outs]
     for (b, h) in heads:
         sl = lambda a: to_f64(a[b:b + 1, h:h + 1])
-        Q, K, V, dO = sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["do"])
+        Q, K, V = sl(x["q"]), sl(x["k"]), sl(x["v"])
         t0 = time.perf_counter()
-        O_ref, lse_ref = attention_fwd(Q, K, V, w.scale, w.causal)
-        dQ, dK, dV = attention_bwd(Q, K, V, dO, w.scale, w.causal)
+        refs = list(attention_fwd(Q, K, V, w.scale, w.causal))
+        if backward:
+            refs += list(attention_bwd(Q, K, V, sl(x["do"]), w.scale, w.causal))
         t += time.perf_counter() - t0
-        worst["O"] = max(worst["O"], float(np.abs(o[b:b + 1, h:h + 1] - O_ref).max()))
-        worst["lse"] = max(worst["lse"], float(np.abs(lse[b:b + 1, h:h + 1] - lse_ref).max()))
-        for n, G, R in (("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
-            rel = float(np.abs(G[b:b + 1, h:h + 1] - R).max() / np.abs(R).max())
-            worst[n] = max(worst[n], rel)
-    credited = 3.5 * fwd_flops(1, 1, w.N, w.d, w.causal) * len(heads)
+        for (n, G, R) in zip(worst, outs, refs):
+            err = float(np.abs(G[b:b + 1, h:h + 1] - R).max())
+            if n not in ("O", "lse"):  # gradients: relative to the max-norm
+                err /= float(np.abs(R).max())
+            worst[n] = max(worst[n], err)
+    credited = (3.5 if backward else 1.0) * fwd_flops(1, 1, w.N, w.d, w.causal) * len(heads)
     return {
         "value": credited / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"fwd+bwd of {len(heads)} whole heads (b,h) in {heads[:3]}... of the workload, "
+        "sample": f"{'fwd+bwd' if backward else 'fwd'} of {len(heads)} whole heads (b,h) in {heads[:3]}"
+                  f"{'...' if len(heads) > 3 else ''} of the workload, "
                   f"N={w.N}, d={w.d}, fp64 numpy; credited FLOPs as for the GPU; {t:.1f} s",
         "seconds": t,
-    }, {"O_maxabs": worst["O"], "lse_maxabs": worst["lse"], "dQ_rel": worst["dQ"],
-        "dK_rel": worst["dK"], "dV_rel": worst["dV"], "heads": len(heads)}
+    }, {(n + ("_maxabs" if n in ("O", "lse") else "_rel")): e for n, e in worst.items()} | {"heads": len(heads)}
 
 
 def decode_measure(dev, steps: int, warmup: int, cpu: bool):
@@ -204,10 +206,11 @@ def _pct(tflops: float) -> dict:
             "pct_of_2516.6": round(100 * tflops / PEAK_ALT, 2)}
 
 
-def configs_measure(dev, steps: int, warmup: int, headline_name: str, headline: dict) -> dict:
+def configs_measure(dev, steps: int, warmup: int, headline_name: str, headline: dict, cpu: bool) -> dict:
     """Every workload of the input recipe at full size: forward (and backward where the
-    workload has one) time, TFLOP/s against both peak figures, and the clock sampled
-    while it ran.  The headline layer's line comes from the main measurement."""
+    workload has one) time, TFLOP/s against both peak figures, the clock sampled while it
+    ran and, with the CPU leg on, the errors of its last head against the oracle.  The
+    headline layer's line comes from the main measurement."""
     import torch
 
     from exact_io_aware_14_amd import fa
@@ -220,8 +223,6 @@ def configs_measure(dev, steps: int, warmup: int, headline_name: str, headline: 
         if name == headline_name:
             out[name] = headline
             continue
-        if w.dtype != "bf16":  # the fp32 tiny case is a parity case, not a rate
-            continue
         x = make_inputs(w, with_do=True)
         q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
         o, lse = fa.fwd(q, k, v, w.scale, w.causal)
@@ -230,6 +231,16 @@ def configs_measure(dev, steps: int, warmup: int, headline_name: str, headline: 
         calls = [lambda: fa.fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)]
         if w.backward:
             calls.append(lambda: fa.bwd(q, k, v, o, do, lse, w.scale, w.causal, workspace=ws, grads=grads))
+        par = None
+        if cpu:  # the last head of the workload against the oracle
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            _, par = cpu_baseline(x, w, [(w.B - 1, w.H - 1)], (o, lse) + (grads if w.backward else ()))
+        if w.dtype != "bf16":  # the fp32 tiny case is a parity case, not a rate
+            out[name] = {"workload": {"B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
+                                      "dtype": w.dtype}, "parity_sample": par}
+            continue
         times = _timed(calls, steps, warmup)
 
         def one_step():
@@ -244,6 +255,8 @@ def configs_measure(dev, steps: int, warmup: int, headline_name: str, headline: 
             rec["bwd"] = _pct(bf / times[1] / 1e9)
             rec["fwd_bwd"] = _pct((ff + bf) / (times[0] + times[1]) / 1e9)
         rec["clock"] = clock
+        if par is not None:
+            rec["parity_sample"] = par
         out[name] = rec
         del x, q, k, v, do, o, lse, ws, grads
     return out
@@ -603,13 +616,15 @@ def main(argv=None) -> int:
         cb, par = cpu_baseline(x, w, heads, (o, lse) + grads)
         rec["cpu_baseline"] = cb
         rec["parity_sample"] = par
+        headline["parity_sample"] = par
     else:
         rec["cpu_baseline"] = None
     if not args.no_next:
         rec["next_rows"] = {"splitkv_decode": decode_measure(dev, args.steps, args.warmup, args.cpu_heads > 0)}
         rec["next_rows"].update(ex_measure(dev, min(args.steps, 10), min(args.warmup, 3), args.cpu_heads > 0))
         rec["secondary"] = secondary_measure(dev, min(args.steps, 10), min(args.warmup, 3))
-        rec["configs"] = configs_measure(dev, min(args.steps, 10), min(args.warmup, 3), w.name, headline)
+        rec["configs"] = configs_measure(dev, min(args.steps, 10), min(args.warmup, 3), w.name, headline,
+                                         args.cpu_heads > 0)
     print(json.dumps(rec), flush=True)
     return 0
 
