@@ -22,11 +22,12 @@
 // * One wave per SIMD (K, V, dK and dV alone hold 192 registers per lane at
 //   d = 128, and as many for the two key blocks of a wave at d = 64, all in AGPRs), so
 //   the overlap comes from inside the wave: the loop is
-//   software pipelined.  Step i starts the S and dP products of tile i from Q/dO
-//   rows already in AGPRs; while they run it reads tile i-1's dO and Q transposed
-//   and tile i's lse and D; then tile i-1's dV/dK products alternate with slices of
-//   tile i's softmax (P and dS on the vector ALUs, kept as bf16 for the next step)
-//   and with the reads of tile i+1's rows into AGPRs.
+//   software pipelined.  Step i runs tile i's S products from Q rows already in
+//   AGPRs, with the step's LDS reads (tile i-1's dO and Q transposed, tile i's lse and
+//   D) under them; then its dP products, with most of P = 2^(S*scale*log2e - lse2) on
+//   the vector ALUs under those; then tile i-1's dV/dK products alternate with the
+//   rest of tile i's softmax (dS, and both kept as bf16 for the next step) and with
+//   the reads of tile i+1's rows into AGPRs.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -268,9 +269,10 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     bf16x8_t bg[2][NDT], bq[2][NDT];
     float lv[16], dvv[16];
     constexpr int NTR = 4 * NDT;        // transposed 16-byte operands to read
-    constexpr int TPK = NTR / NKK;      // ... per d-step of the products
-    constexpr int LPK = 8 / NKK;        // lse/D 128-bit reads per d-step
-    static_assert(NTR % NKK == 0 && 8 % NKK == 0, "reads must split over the d-steps");
+    constexpr int NRD = NKK < 4 ? NKK : 4;  // d-steps the reads are spread over
+    constexpr int TPK = NTR / NRD;      // ... per d-step of the products
+    constexpr int LPK = 8 / NRD;        // lse/D 128-bit reads per d-step
+    static_assert(NTR % NRD == 0 && 8 % NRD == 0, "reads must split over the d-steps");
     auto read_tr = [&](int t) {  // t = (j * NDT + dt) * 2 + (0: dO, 1: Q)
       const int j = t / (2 * NDT), dt = (t / 2) % NDT;
       const __bf16* b = (t & 1) ? Qp : Gp;
@@ -284,56 +286,81 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       float* dst = (t & 1) ? dvv : lv;
       dst[4 * b] = x.x, dst[4 * b + 1] = x.y, dst[4 * b + 2] = x.z, dst[4 * b + 3] = x.w;
     };
+    // S = Q K^T alone first: its chain of dependent products runs back to back.  The
+    // step's LDS reads go under it.
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
 #pragma unroll
       for (int b = 0; b < KB; ++b) {
-        if (kk == 0) {
-          mma_v_first_aa(s[b], aq[0], kop[b][0]);
-          mma_v_first_aa(dp[b], ag[0], vop[b][0]);
-        } else {
-          mma_v_aa(s[b], aq[kk], kop[b][kk]);
-          mma_v_aa(dp[b], ag[kk], vop[b][kk]);
-        }
+        if (kk == 0) mma_v_first_aa(s[b], aq[0], kop[b][0]);
+        else mma_v_aa(s[b], aq[kk], kop[b][kk]);
       }
+      if (kk < NRD) {
 #pragma unroll
-      for (int t = kk * TPK; t < kk * TPK + TPK; ++t) read_tr(t);
+        for (int t = kk * TPK; t < kk * TPK + TPK; ++t) read_tr(t);
 #pragma unroll
-      for (int t = kk * LPK; t < kk * LPK + LPK; ++t) read_le(t);
+        for (int t = kk * LPK; t < kk * LPK + LPK; ++t) read_le(t);
+      }
       // tile qt+2 starts loading once the first products are under way
       if (kk == 1 && qt + 2 < nqt) issue_q(qt + 2, Qi, Gi, Li, Ei);
       __builtin_amdgcn_sched_barrier(0);
     }
-    mfma_v_ready(s[KB - 1], dp[KB - 1]);
+    // Then dP = dO V^T, with P = 2^(s*c - lse2) of the first N1 elements on the vector
+    // ALUs under it (element e is row 8 * (e / (8*KB)) + e % 8 of key block (e / 8) % KB).
+    constexpr int NDP = NKK * KB;
+    constexpr int N1 = 2 * (NDP - 2) < 16 * KB ? 2 * (NDP - 2) : 16 * KB;
+    // Keys past the end and, on tiles crossing the diagonal, keys above it: S = -inf,
+    // so P = 2^-inf = 0 and dS = 0.  Only those tiles pay for the per-element test.
+    const bool need_mask = (kw + 32 * KB > N) || (causal && kw + 32 * KB - 1 > qb0) ||
+                           (window > 0 && qb0 + 31 >= kw + window);
 #pragma unroll
-    for (int b = 0; b < KB - 1; ++b) asm volatile("" : "+v"(s[b]), "+v"(dp[b]));  // after the wait states
+    for (int m = 0; m < NDP; ++m) {
+      const int kk = m / KB, b = m % KB;
+      if (kk == 0) mma_v_first_aa(dp[b], ag[0], vop[b][0]);
+      else mma_v_aa(dp[b], ag[kk], vop[b][kk]);
+      if (m == 1) {  // two products after the last of S: its wait states run under them
+        mfma_v_ready1(s[KB - 1]);
+#pragma unroll
+        for (int bb = 0; bb < KB - 1; ++bb) asm volatile("" : "+v"(s[bb]));
+        if (need_mask) {
+#pragma unroll
+          for (int bb = 0; bb < KB; ++bb) {
+            const int key = kw + 32 * bb + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int q = qb0 + crow(g, r);
+              const bool dead = (key >= N) | (causal & (key > q)) | ((window > 0) & (q - key >= window));
+              s[bb][r] = dead ? -INFINITY : s[bb][r];
+            }
+          }
+        }
+      }
+      if (m >= 2) {
+#pragma unroll
+        for (int e = 2 * (m - 2); e < 2 * (m - 2) + 2 && e < N1; ++e) {
+          const int eb = (e / 8) % KB, r = 8 * (e / (8 * KB)) + e % 8;
+          s[eb][r] = __builtin_amdgcn_exp2f(fmaf(s[eb][r], c, -lv[r]));
+          asm volatile("" : "+v"(s[eb][r]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
     // All of this phase's LDS reads (transposed operands, lse, D) are waited for here,
     // before the next tile's row reads below are issued: those are inline assembly the
     // compiler does not count, so a wait it places later for one of this phase's reads
     // would also wait for them.
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-
-    // Keys past the end and, on tiles crossing the diagonal, keys above it: S = -inf,
-    // so P = 2^-inf = 0 and dS = 0.  Only those tiles pay for the per-element test.
-    if ((kw + 32 * KB > N) || (causal && kw + 32 * KB - 1 > qb0) ||
-        (window > 0 && qb0 + 31 >= kw + window)) {
+    // The first dV product reads neither S nor dP: it runs while dP's last products
+    // drain, under the wait states the vector ALUs need before reading them.
+    mma_a(dv[0][0], pa[0][0], bg[0][0]);
+    mfma_v_ready1(dp[KB - 1]);
 #pragma unroll
-      for (int b = 0; b < KB; ++b) {
-        const int key = kw + 32 * b + l32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int q = qb0 + crow(g, r);
-          const bool dead = (key >= N) | (causal & (key > q)) | ((window > 0) & (q - key >= window));
-          s[b][r] = dead ? -INFINITY : s[b][r];
-        }
-      }
-    }
+    for (int b = 0; b < KB - 1; ++b) asm volatile("" : "+v"(dp[b]));  // after the wait states
 
     // The previous tile's dV/dK products (accumulating in AGPRs), each followed by
     // elements of this tile's P = 2^(s*c - lse2) and dS = P (dP - D) on the vector
     // ALUs and by reads of the next tile's rows; sched_barrier keeps that interleave.
     constexpr int NSTEP = 2 * NDT * KB, EPS = 16 * KB / NSTEP;  // product pairs; elements per pair
-    constexpr int RPS = (NKK + NSTEP - 1) / NSTEP;    // row-operand steps read per pair
     // Each slice's P and dS are pinned where they are computed (empty asm reading
     // them): the compiler would otherwise sink the dS arithmetic and the bf16
     // conversions below the last product, where they run with the matrix cores idle.
@@ -355,22 +382,32 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     // is row 8 * (e / (8*KB)) + e % 8 of key block (e / 8) % KB, so the first NSTEP/2
     // pairs both read and (by their end) compute exactly query half 0.
     static_assert(EPS * (NSTEP / 2) == 8 * KB && NSTEP / 2 == NDT * KB, "half 0 is done by slot NSTEP/2");
+    // Row reads of the next tile go in the first half of the pairs, so they are back
+    // well before the next step's wait.
+    constexpr int RPP = (NKK + NSTEP / 2 - 1) / (NSTEP / 2);  // row-operand steps per pair
+    auto elems = [&](int e0, int e1) {  // P of elements below N1 is already formed
 #pragma unroll
-    for (int i = 0; i < NSTEP; ++i) {
-      const int j = i / (NDT * KB), b = (i / NDT) % KB, dt = i % NDT;
-      mma_a(dv[b][dt], pa[b][j], bg[j][dt]);
-      mma_a(dk[b][dt], da[b][j], bq[j][dt]);
-#pragma unroll
-      for (int kk = i * RPS; kk < i * RPS + RPS && kk < NKK; ++kk) prefetch_rows(Qn, Gn, kk);
-      if (i == NSTEP / 2) to_bf16(0);  // products 0 .. NSTEP/2-1 read half 0
-#pragma unroll
-      for (int e = i * EPS; e < i * EPS + EPS; ++e) {
+      for (int e = e0; e < e1; ++e) {
         const int b = (e / 8) % KB, r = 8 * (e / (8 * KB)) + e % 8;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lv[r]));
+        const float p = e < N1 ? s[b][r] : __builtin_amdgcn_exp2f(fmaf(s[b][r], c, -lv[r]));
         s[b][r] = p;
         dp[b][r] = p * (dp[b][r] - dvv[r]);
         asm volatile("" : "+v"(s[b][r]), "+v"(dp[b][r]));
       }
+    };
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      const int j = i / (NDT * KB), b = (i / NDT) % KB, dt = i % NDT;
+      // Each product is followed by half the pair's vector work, so both products of
+      // the pair run under it.
+      if (i > 0) mma_a(dv[b][dt], pa[b][j], bg[j][dt]);
+      if (i == NSTEP / 2) to_bf16(0);  // products 0 .. NSTEP/2-1 read half 0
+      elems(i * EPS, i * EPS + EPS / 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma_a(dk[b][dt], da[b][j], bq[j][dt]);
+#pragma unroll
+      for (int kk = i * RPP; kk < i * RPP + RPP && kk < NKK; ++kk) prefetch_rows(Qn, Gn, kk);
+      elems(i * EPS + EPS / 2, i * EPS + EPS);
       __builtin_amdgcn_sched_barrier(0);
     }
     to_bf16(1);

@@ -230,9 +230,9 @@ __device__ __forceinline__ void lds_read_a_pair(bf16x8_t& d0, bf16x8_t& d1, cons
   const unsigned addr = lds_addr(p);
   asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:%3" : "=&a"(d0), "=a"(d1) : "v"(addr), "i"(OFF) : "memory");
 }
-// MFMA results in VGPRs may now be touched by vector code.
-__device__ __forceinline__ void mfma_v_ready(f32x16_t& x, f32x16_t& y) {
-  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
+// An MFMA result in VGPRs may now be touched by vector code.
+__device__ __forceinline__ void mfma_v_ready1(f32x16_t& x) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x));
 }
 // Vector-written MFMA operands in VGPRs may now be read by an MFMA.
 __device__ __forceinline__ void valu_ready(bf16x8_t& a, bf16x8_t& b, bf16x8_t& c, bf16x8_t& d) {
