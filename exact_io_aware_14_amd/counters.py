@@ -8,6 +8,7 @@ once after a warm-up step::
 
     rocprofv3 --pmc <PASSES["busy"]> -f csv -d <dir>/busy -o p -- python -u bench.py --traffic-run [--workload W]
     rocprofv3 --pmc <PASSES["mix"]>  -f csv -d <dir>/mix  -o p -- python -u bench.py --traffic-run [--workload W]
+    rocprofv3 --pmc <PASSES["stall"]> -f csv -d <dir>/stall -o p -- python -u bench.py --traffic-run [--workload W]
     rocprofv3 --kernel-trace --stats -d <dir>/trace -o p -- python -u bench.py --traffic-run [--workload W]
     python -m exact_io_aware_14_amd.counters <dir> --workload W [--out profiles/counters_W.md]
 
@@ -25,6 +26,11 @@ checked against the runs):
   of a CU; 100 x value / (256 CUs x elapsed cycles) is the ``VALUBusy`` metric: the
   share of cycles a SIMD spends issuing vector (resp. LDS) instructions.
 * SQ_LDS_IDX_ACTIVE / (256 x elapsed cycles): the share of cycles each CU's LDS is busy.
+* Where a wave's cycles go (the optional stall pass), as shares of SQ_WAVE_CYCLES:
+  SQ_WAIT_ANY (waiting on a counter or the barrier), SQ_WAIT_INST_ANY (ready but waiting
+  to issue: a dependency or a busy unit) and SQ_ACTIVE_INST_ANY (issuing); and
+  SQ_VALU_MFMA_COEXEC_CYCLES over the vector-busy cycles 4 x SQ_ACTIVE_INST_VALU: the
+  share of vector work that runs while the wave's MFMA work does.
 """
 from __future__ import annotations
 
@@ -46,6 +52,9 @@ PASSES = {
     "mix": ["GRBM_GUI_ACTIVE", "SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU",
             "SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
             "SQ_WAIT_INST_LDS", "SQ_WAIT_INST_ANY"],
+    "stall": ["GRBM_GUI_ACTIVE", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+              "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_ACTIVE_INST_VALU2", "SQ_INSTS_VMEM_RD",
+              "SQ_ACTIVE_INST_SCA", "SQ_WAVE_CYCLES"],
 }
 
 # kernel-name fragments -> label (the first fragment found in a name wins)
@@ -143,10 +152,25 @@ def summarize(dirpath: str, workload: str) -> str:
                     f"{frac:.1f} | {valu:.1f} | {lds_issue:.1f} | {lds_unit:.1f} | "
                     f"{m.get('SQ_INSTS_LDS', float('nan')) / nm:.2f} | {m.get('SQ_INSTS_VALU', float('nan')) / nm:.2f} | "
                     f"{m.get('SQ_INSTS_VALU_TRANS_F32', float('nan')) / nm:.2f} | {conflict:.2f} |")
+    stall_dir = os.path.join(dirpath, "stall")
+    stall = read_pass(stall_dir) if os.path.isdir(stall_dir) else {}
+    if stall:
+        rows += ["", "Where the waves' cycles go (stall pass; shares of `SQ_WAVE_CYCLES`; the last column is",
+                 "`SQ_VALU_MFMA_COEXEC_CYCLES` over the vector-busy cycles `4 x SQ_ACTIVE_INST_VALU`):", "",
+                 "| kernel | waiting for anything | waiting to issue | issuing | VALU cycles that overlap MFMA work |",
+                 "|---|---|---|---|---|"]
+        for lab in [l for _, l in KERNELS]:
+            if lab not in stall or lab not in busy or busy[lab].get("SQ_INSTS_MFMA", 0.0) == 0.0:
+                continue
+            s, b = stall[lab], busy[lab]
+            wc = s["SQ_WAVE_CYCLES"]
+            rows.append(f"| {lab} | {100 * s['SQ_WAIT_ANY'] / wc:.0f} % | {100 * s['SQ_WAIT_INST_ANY'] / wc:.0f} % | "
+                        f"{100 * s['SQ_ACTIVE_INST_ANY'] / wc:.0f} % | "
+                        f"{100 * s['SQ_VALU_MFMA_COEXEC_CYCLES'] / (4 * b['SQ_ACTIVE_INST_VALU']):.0f} % |")
     raw = ["", "Raw counters (mean per dispatch; GRBM_GUI_ACTIVE summed over the 8 XCDs):", "",
            "| kernel | counter | value |", "|---|---|---|"]
     for lab in [l for _, l in KERNELS]:
-        for src in (busy, mix):
+        for src in (busy, mix, stall):
             for c, v in sorted(src.get(lab, {}).items()):
                 raw.append(f"| {lab} | {c} | {v:.6g} |")
     return "\n".join(rows + raw) + "\n"
