@@ -83,11 +83,20 @@ def cpu_baseline(x, w, heads, outs):
                 err /= float(np.abs(R).max())
             worst[n] = max(worst[n], err)
     credited = (3.5 if backward else 1.0) * fwd_flops(1, 1, w.N, w.d, w.causal) * len(heads)
+    naive = (3.5 if backward else 1.0) * fwd_flops(1, 1, w.N, w.d, False) * len(heads)  # full N^2
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {
         "value": credited / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
+        "naive_flop_tflops": naive / t / 1e12,
+        "cpu_model": cpu,
         "sample": f"{'fwd+bwd' if backward else 'fwd'} of {len(heads)} whole heads (b,h) in {heads[:3]}"
                   f"{'...' if len(heads) > 3 else ''} of the workload, "
                   f"N={w.N}, d={w.d}, fp64 numpy; credited FLOPs as for the GPU; {t:.1f} s",
