@@ -186,6 +186,22 @@ def test_fwd_bitwise_deterministic(dev):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_bf16_bwd_bitwise_deterministic(dev, d):
+    """The bf16 backward accumulates without atomics: two runs agree bit for bit (the fp32
+    path's dQ atomics may differ in the last bits)."""
+    w = Workload("detb", 2, 3, 555, d, True, "bf16", True, seed=6)
+    say(f"[determinism] bf16 bwd twice, d={d}")
+    x = make_inputs(w, with_do=True)
+    q, k, v, o, lse = gpu_fwd(x, w, dev)
+    do = x["do"].to(dev)
+    g1 = gpu_bwd(q, k, v, o, lse, do, w, dev)
+    g2 = gpu_bwd(q, k, v, o, lse, do, w, dev)
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_invalid_arguments_fail_loudly(dev):
     say("[errors] invalid arguments through the C ABI")
     q = torch.randn(1, 1, 64, 96, device=dev, dtype=torch.bfloat16)
