@@ -210,7 +210,8 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads, fused: bool
     """The backward as separate calls (same result as :func:`bwd`), returned as a list of
     callables so a caller can time or interleave them.  ``fused=False``: the three stages
     fa_bwd_preprocess, fa_bwd_main, fa_bwd_dq.  ``fused=True``: the launches fa_bwd itself
-    makes (bf16: fa_bwd_dq_pre, then fa_bwd_main; fp32: the three stages)."""
+    makes, one call each through fa_bwd_ex_launches (bf16: the dQ pass with the
+    preprocess folded in, then the dK/dV pass; fp32: the three stages)."""
     _check_same(q, k, v, o, do)
     B, H, N, d = _dims(q)
     _out(lse, (B, H, N), torch.float32, q.device, "lse")
@@ -237,14 +238,17 @@ def bwd_stages(q, k, v, o, do, lse, scale, causal, workspace, grads, fused: bool
         if r != FA_OK:
             raise FaError(r, "fa_bwd_dq")
 
-    def dq_pre():
-        r = L.fa_bwd_dq_pre(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                            lse.data_ptr(), dq.data_ptr(), wp, wn, B, H, N, d, sc, ca, dt, st)
-        if r != FA_OK:
-            raise FaError(r, "fa_bwd_dq_pre")
+    def launch(mask):
+        def run():
+            r = L.fa_bwd_ex_launches(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), wp, wn,
+                                     None, B, H, N, 0, d, sc, ca, 0, dt, mask, st)
+            if r != FA_OK:
+                raise FaError(r, "fa_bwd_ex_launches")
+        return run
 
     if fused and q.dtype == torch.bfloat16:
-        return [dq_pre, main]
+        return [launch(1), launch(2)]
     return [pre, main, dqs]
 
 

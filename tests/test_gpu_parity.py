@@ -258,9 +258,10 @@ def test_memory_stays_linear_long_context(dev):
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_bwd_stages_equal_fa_bwd(dev, dtype, d):
-    """fa_bwd_preprocess + fa_bwd_main + fa_bwd_dq, and fa_bwd's own launches
-    (bf16: fa_bwd_dq_pre with the preprocess folded in, then fa_bwd_main), reproduce
-    fa_bwd bit for bit (fp32 dQ: up to its atomics' summation order)."""
+    """fa_bwd_preprocess + fa_bwd_main + fa_bwd_dq, fa_bwd's own launches one by one
+    through fa_bwd_ex_launches (bf16: the dQ pass with the preprocess folded in, then the
+    dK/dV pass) and, for bf16, the entry points fa_bwd_dq_pre then fa_bwd_main all
+    reproduce fa_bwd bit for bit (fp32 dQ: up to its atomics' summation order)."""
     w = Workload("stages", 1, 3, 500, d, True, dtype, True, seed=7)
     say(f"[stages] bwd in separate calls vs one, {dtype} d={d}")
     x = make_inputs(w)
@@ -280,6 +281,18 @@ def test_bwd_stages_equal_fa_bwd(dev, dtype, d):
             assert torch.equal(dq1, dq2), f"fused={fused}"
         else:
             check_grad("fp32", dq2, f64(dq1), "dQ", "stages")
+    if dtype == "bf16":
+        L, st = fa.lib(), torch.cuda.current_stream().cuda_stream
+        ws = torch.full((fa.workspace_bytes(w.B, w.H, w.N, w.d, q.dtype),), 0xFF, dtype=torch.uint8, device=dev)
+        dq3, dk3, dv3 = (torch.full_like(q, float("nan")) for _ in range(3))
+        P = lambda t: t.data_ptr()
+        wn = ws.numel()
+        assert L.fa_bwd_dq_pre(P(q), P(k), P(v), P(o), P(do), P(lse), P(dq3), P(ws), wn, w.B, w.H, w.N, w.d,
+                               w.scale, 1, fa.FA_DTYPE_BF16, st) == fa.FA_OK
+        assert L.fa_bwd_main(P(q), P(k), P(v), P(do), P(dk3), P(dv3), P(ws), wn, w.B, w.H, w.N, w.d,
+                             w.scale, 1, fa.FA_DTYPE_BF16, st) == fa.FA_OK
+        torch.cuda.synchronize()
+        assert torch.equal(dq1, dq3) and torch.equal(dk1, dk3) and torch.equal(dv1, dv3)
 
 
 def test_calls_run_on_the_current_stream(dev):
