@@ -235,6 +235,29 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     };
     scores();
 
+    // V^T operand of keys ks*32 + j*16 .. +15 for dim tile dt (two transposed reads).
+    auto read_v = [&](int ks, int j, int dt) -> bf16x8_t {
+      const __bf16* base = Vb + v_rd[dt] + (ks * 32 + j * 16) * D;
+      const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(base));
+      const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) i16x4_t*)(base + 8 * D));
+      bf16x8_t a;
+      const bf16x4_t lob = __builtin_bit_cast(bf16x4_t, lo), hib = __builtin_bit_cast(bf16x4_t, hi);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        a[t] = lob[t];
+        a[4 + t] = hib[t];
+      }
+      return a;
+    };
+    // The operands of the tile's first 16 keys are read before the softmax, so that their
+    // LDS latency passes under it and the PV products can start on its last weight.
+    bf16x8_t vfirst[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) vfirst[dt] = read_v(0, 0, dt);
+    __builtin_amdgcn_sched_barrier(0);
+
     // Online softmax against the lazily moved reference mref: p = 2^(s*c - mref*c).
     // The theorem's exactness needs only one common reference for l and o~, and the
     // reference only has to keep the weights bounded.  So after the first tile the
@@ -245,7 +268,9 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     // reference and the weights are formed again.  The scores for that come from
     // registers of their own at d = 64; at d = 128, where those registers would cost
     // more, the weights overwrite the scores and the rare path computes the scores
-    // again from the K tile still in LDS.
+    // again from the K tile still in LDS.  The first tile and the rare case share one
+    // copy of the reference move; with two, the compiler copied the weights between
+    // register sets on every tile where the paths joined.
     constexpr bool kKeepScores = D == 64;
     f32x16_t pst[kKeepScores ? NKS : 1];
     auto P = [&](int ks) -> f32x16_t& {
@@ -253,6 +278,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
       else return s[ks];
     };
     float t = 0.0f;
+    bool again = first;
     if (!first) {
       const float mc = mref * c;
 #pragma unroll
@@ -262,11 +288,12 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
           P(ks)[r] = __builtin_amdgcn_exp2f(fmaf(s[ks][r], c, -mc));
           t += P(ks)[r];
         }
-    }
-    if (first || __builtin_amdgcn_ballot_w64(!(t <= kWeightBound))) {  // wave-uniform, rare
+      again = __builtin_amdgcn_ballot_w64(!(t <= kWeightBound)) != 0;  // wave-uniform, rare
       if constexpr (!kKeepScores) {
-        if (!first) scores();
+        if (again) scores();
       }
+    }
+    if (again) {
       first = false;
       float mx = s[0][0];
 #pragma unroll
@@ -316,18 +343,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
         lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones2, lsum_bf, false);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const __bf16* base = Vb + v_rd[dt] + (ks * 32 + j * 16) * D;
-          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(base));
-          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4_t*)(base + 8 * D));
-          bf16x8_t a;
-          const bf16x4_t lob = __builtin_bit_cast(bf16x4_t, lo), hib = __builtin_bit_cast(bf16x4_t, hi);
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            a[t] = lob[t];
-            a[4 + t] = hib[t];
-          }
+          const bf16x8_t a = (ks == 0 && j == 0) ? vfirst[dt] : read_v(ks, j, dt);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
         }
       }
