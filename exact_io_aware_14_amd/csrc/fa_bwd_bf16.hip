@@ -1,7 +1,7 @@
 // fa_bwd_bf16.hip -- the bf16 dK/dV pass of the backward, tuned for gfx950.
 //
 // Method ("FlashAttention and online softmax", ML Systems Lesson 4, "Backward pass:
-// recompute instead of store"): one workgroup per block of keys (32 per wave at
+// recompute instead of store"): one workgroup at a time per block of keys (32 per wave at
 // d = 128, two blocks of 32 per wave at d = 64), K_j and V_j in registers, dK_j and dV_j
 // accumulated in registers, query tiles of 32 rows streamed; per tile
 //   S = Q_i K_j^T, P = exp2(S*scale*log2e - lse_i*log2e),  dP = dO_i V_j^T,
@@ -28,6 +28,10 @@
 //   the vector ALUs under those; then tile i-1's dV/dK products alternate with the
 //   rest of tile i's softmax (dS, and both kept as bf16 for the next step) and with
 //   the reads of tile i+1's rows into AGPRs.
+// * Dense calls run one workgroup per CU, each looping over its blocks of keys (a
+//   block's K and V rows are staged in LDS by direct loads and read into AGPRs from
+//   there).  A workgroup stages its next block's rows while it finishes the current
+//   one, so a block starts without a round trip to HBM and without a new dispatch.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int Nmax, int Npad, float scale, int causal,
-    int nkb, SeqMap sm_arg, int window_arg) {
+    int nkb, int total, SeqMap sm_arg, int window_arg) {
   // GEN = false: dense tensors, no window; the general code folds away.
   const int window = GEN ? window_arg : 0;
   const SeqMap sm{GEN ? sm_arg.cu : nullptr, sm_arg.B, sm_arg.T};
@@ -111,25 +115,55 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   __shared__ __attribute__((aligned(16))) float E1[C::BQ];
   __shared__ __attribute__((aligned(16))) float E2[C::BQ];
   __shared__ __attribute__((aligned(16))) float E3[C::BQ];
+  // K and V rows of a block, staged by direct loads and then read into AGPRs: chunk c of
+  // row r (16-byte units) at ((r/16)*CPR + c)*16 + r%16, so the 16 lanes of a 128-bit read
+  // phase, 16 consecutive rows at one chunk, touch 256 contiguous bytes.  A block's rows
+  // are loaded while the block before it ends (see the block loop below).
+  __shared__ __attribute__((aligned(1024))) __bf16 KVs[2 * C::BKV * D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
-  const int id = xcd_remap(blockIdx.x, gridDim.x);
-  int bh = id / nkb, kb = id - bh * nkb;
-  if (causal) {  // the first key blocks see the most query tiles: heaviest first
-    int t;
-    heavy_first(id, nkb, gridDim.x / nkb, GEN ? 1 : heavy_group(Nmax, D), bh, t);
-    kb = nkb - 1 - t;
-  }
-  int base, N;  // first row and length of this (batch, head)
-  seq_rows(sm, bh, Nmax, base, N);
-  const size_t head = (size_t)base * D;
-  const size_t hpad = (size_t)bh * Npad;
-  const int k0 = kb * C::BKV;
-  if (k0 >= N) return;  // a short sequence of a variable-length batch: no keys here
   constexpr int KB = C::KB;
-  const int kw = k0 + w * 32 * KB;  // this wave's first key
+  // Logical blocks (id: unit and key block, heaviest first when causal) are taken in
+  // rounds k = 0, 1, ... of nwg = gridDim.x at a time.  A launch of one workgroup per block
+  // runs one round.  A persistent launch (fewer workgroups, each looping) walks every
+  // second round backwards within its XCD (nwg a multiple of 8), so a workgroup's blocks
+  // alternate between the heavy and the light end of a round; blocks stay on the XCD
+  // whose L2 holds their unit's rows, as with one workgroup per block.
+  const int nwg = gridDim.x;
+  auto vindex = [&](int k) -> int {
+    const int wi = blockIdx.x;
+    if ((nwg & 7) != 0 || !(k & 1)) return k * nwg + wi;
+    return k * nwg + (nwg - 8 - (wi & ~7)) + (wi & 7);
+  };
+  auto block_of = [&](int v, int& bh_, int& kb_) {
+    const int id = xcd_remap(v, total);
+    bh_ = id / nkb;
+    kb_ = id - bh_ * nkb;
+    if (causal) {  // the first key blocks see the most query tiles: heaviest first
+      int t;
+      heavy_first(id, nkb, total / nkb, GEN ? 1 : heavy_group(Nmax, D), bh_, t);
+      kb_ = nkb - 1 - t;
+    }
+  };
+  // The current block: unit bh, rows base.. of its sequence (length N), keys k0.. (this
+  // wave's from kw), query tiles qt0..nqt-1.
+  int bh = 0, kb = 0, base = 0, N = 0, k0 = 0, kw = 0, nqt = 0, qt0 = 0;
+  size_t head = 0, hpad = 0;
+  auto set_block = [&](int v) {
+    block_of(v, bh, kb);
+    seq_rows(sm, bh, Nmax, base, N);
+    head = (size_t)base * D;
+    hpad = (size_t)bh * Npad;
+    k0 = kb * C::BKV;
+    kw = k0 + w * 32 * KB;
+    // query tiles of this sequence (its padded rows hold lse = +inf: P = 0 there) ...
+    nqt = (N + C::BQ - 1) / C::BQ;
+    qt0 = causal ? k0 / C::BQ : 0;  // ... earlier rows see none of these keys
+    if (window > 0)  // ... nor do rows past the last key's band
+      nqt = min(nqt, (k0 + C::BKV - 1 + window - 1) / C::BQ + 1);
+  };
 
   // --- direct-load source offsets ------------------------------------------------
   // Row-major swizzled tiles: chunk slot s = r*CPR + p holds logical chunk p ^ f(r).
@@ -178,62 +212,92 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       trq[h][dt] = row * D + ((((col >> 3) ^ bswz<D>(row))) << 3) + (col & 7);
     }
 
-  // --- K and V of this wave's keys as B operands (natural k order) in registers --
-  bf16x8_t kop[KB][NKK], vop[KB][NKK];
-#pragma unroll
-  for (int b = 0; b < KB; ++b)
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int key = kw + 32 * b + l32;
-      if (key < N) {
-        const int off = (key - k0) * D + kk * 16 + g * 8;  // from the block's first key
-        kop[b][kk] = *reinterpret_cast<const bf16x8_t*>(K + head + (size_t)k0 * D + off);
-        vop[b][kk] = *reinterpret_cast<const bf16x8_t*>(V + head + (size_t)k0 * D + off);
-      } else {
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          kop[b][kk][t] = (__bf16)0.0f;
-          vop[b][kk][t] = (__bf16)0.0f;
-        }
-      }
-    }
-
+  // --- K and V of this wave's keys as B operands (natural k order), in AGPRs -------
   // K and V only ever feed the matrix cores, which read A/B operands from AGPRs as
   // well; keeping them there leaves the VGPRs for operand prefetch.
+  bf16x8_t kop[KB][NKK], vop[KB][NKK];
+  constexpr int KVL = C::BKV * CPR / 64 / C::NW;  // direct loads per wave and tensor
+  static_assert(C::BKV * CPR % (64 * C::NW) == 0, "K/V rows split over the waves");
+  // Stage keys kk0.. of the unit whose rows start at element hd (sequence length n); rows
+  // past the end read the last row (their S is masked, so P = 0 and dS = 0 there).
+  auto issue_kv = [&](size_t hd, int kk0, int n) {
+    // The bases come out of this block's index arithmetic right here, partly on the vector
+    // ALUs: wait states between their last write and the loads.
+    const unsigned long long ks = sgpr_ptr(K + hd + (size_t)kk0 * D);
+    const unsigned long long vs = sgpr_ptr(V + hd + (size_t)kk0 * D);
+    sgpr_wait(ks, vs);
+    // the lane index read afresh, so that no offset stays live across the steps
+    unsigned ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
 #pragma unroll
-  for (int b = 0; b < KB; ++b)
+    for (int i = 0; i < KVL; ++i) {
+      const int slot = (w * KVL + i) * 64 + (int)ln;
+      const int grp = slot / (CPR * 16), within = slot % (CPR * 16);
+      const int r = min(grp * 16 + (within & 15), n - 1 - kk0);
+      const unsigned off = (unsigned)(r * D + (within >> 4) * 8) * 2u;
+      dma16_s(ks, off, KVs + (w * KVL + i) * 64 * 8);
+      dma16_s(vs, off, KVs + C::BKV * D + (w * KVL + i) * 64 * 8);
+    }
+  };
+  // The staged rows into AGPRs (then waited for: lgkmcnt(0)).
+  auto read_kv = [&]() {
+    unsigned ln;  // read afresh, as in issue_kv
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int l32f = (int)ln & 31, gf = (int)ln >> 5;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) asm volatile("s_nop 3" : "+a"(kop[b][kk]), "+a"(vop[b][kk]));
+    for (int b = 0; b < KB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int r = w * 32 * KB + 32 * b + l32f, c = 2 * kk + gf;
+        const int e = (((r >> 4) * CPR + c) * 16 + (r & 15)) * 8;
+        lds_read_a(kop[b][kk], KVs + e);
+        lds_read_a(vop[b][kk], KVs + C::BKV * D + e);
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  };
+  // The next block's rows (round kcur + 1) are staged right after this block's last
+  // tile load: they load under its last steps, products and stores, whose waits leave
+  // those KVN loads in flight (kv_inflight).
+  constexpr int KVN = 2 * KVL;
+  static_assert(KVN < 64, "vmcnt range");
+  int kcur = 0;
+  bool kv_inflight = false;
+  auto issue_kv_next = [&]() {
+    int bhn, kbn, basen, nn;
+    block_of(vindex(kcur + 1), bhn, kbn);
+    seq_rows(sm, bhn, Nmax, basen, nn);
+    issue_kv((size_t)basen * D, kbn * C::BKV, nn);
+  };
+
   // dK^T, dV^T accumulators in AGPRs (written by v_accvgpr_write: 4 wait states
   // before the first product accumulates into them).
   f32x16_t dk[KB][NDT], dv[KB][NDT];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int b = 0; b < KB; ++b)
+    for (int b = 0; b < KB; ++b)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      dk[b][dt] = zero16();
-      dv[b][dt] = zero16();
-      asm volatile("s_nop 3" : "+a"(dk[b][dt]), "+a"(dv[b][dt]));
-    }
+      for (int dt = 0; dt < NDT; ++dt) {
+        dk[b][dt] = zero16();
+        dv[b][dt] = zero16();
+        asm volatile("s_nop 3" : "+a"(dk[b][dt]), "+a"(dv[b][dt]));
+      }
+  };
   const float c = scale * kLog2e;
-  // query tiles of this sequence (its padded rows hold lse = +inf: P = 0 there) ...
-  int nqt = (N + C::BQ - 1) / C::BQ;
-  const int qt0 = causal ? k0 / C::BQ : 0;  // ... earlier rows see none of these keys
-  if (window > 0)  // ... nor do rows past the last key's band
-    nqt = min(nqt, (k0 + C::BKV - 1 + window - 1) / C::BQ + 1);
 
   // P^T and dS^T of the previous tile, as bf16 A operands (j = 0, 1 query halves).
   // They start at zero, so the first step's dV/dK products add nothing.
   bf16x8_t pa[KB][2], da[KB][2];
+  auto zero_pd = [&]() {
 #pragma unroll
-  for (int b = 0; b < KB; ++b)
+    for (int b = 0; b < KB; ++b)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        pa[b][j][t] = (__bf16)0.0f;
-        da[b][j][t] = (__bf16)0.0f;
-      }
+        for (int t = 0; t < 8; ++t) {
+          pa[b][j][t] = (__bf16)0.0f;
+          da[b][j][t] = (__bf16)0.0f;
+        }
+  };
   // Q and dO rows of the next tile (A operands of its S and dP), read one step ahead
   // straight into AGPRs: the S and dP products of a step then start right after its
   // barrier, and these reads run under the previous step's dV/dK products.
@@ -255,7 +319,10 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   auto step = [&](int qt, const __bf16* Qp, const __bf16* Gp, const float* Lc, const float* Ec,
                   const __bf16* Qn, const __bf16* Gn, __bf16* Qi, __bf16* Gi, float* Li, float* Ei) {
     __builtin_amdgcn_sched_barrier(0);  // no code motion across steps
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    if (kv_inflight)  // all but the next block's K/V rows: vmcnt(KVN) lgkmcnt(0)
+      __builtin_amdgcn_s_waitcnt(((KVN >> 4) << 14) | (KVN & 15) | 0x0070);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const int qb0 = qt * C::BQ;
@@ -415,86 +482,123 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     for (int b = 0; b < KB; ++b) valu_ready(pa[b][0], pa[b][1], da[b][0], da[b][1]);  // read next step
   };
 
-  // Prologue: tiles qt0 and qt0+1 loading, then tile qt0's rows.  The first step reads
-  // its "previous" dV/dK operands from Q3/G3, which nothing has loaded: zero them,
-  // since 0 * (an Inf or NaN bit pattern) would not be 0.  The prologue's barrier
-  // orders these writes before those reads, and the first load into Q3/G3 comes
-  // after the second step's barrier.
+  // Q3/G3 start at zero: the first step of a workgroup's first block reads its "previous"
+  // dV/dK operands there (with P^T = dS^T = 0), and 0 * (an Inf or NaN bit pattern) would
+  // not be 0; later blocks find finite rows of earlier tiles there.  The first block's
+  // barrier orders these writes before those reads.
   for (int i = tid; i < C::QTILE / 8; i += C::NT) {
     reinterpret_cast<v16b*>(Q3)[i] = v16b{0, 0, 0, 0};
     reinterpret_cast<v16b*>(G3)[i] = v16b{0, 0, 0, 0};
   }
-  issue_q(qt0, Q0, G0, L0, E0);
-  if (qt0 + 1 < nqt) issue_q(qt0 + 1, Q1, G1, L1, E1);
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
+  // Every block after a workgroup's first found its K/V rows staged by the one before it:
+  // dense blocks are never empty, and other calls run one round.
+  for (int k = 0;; ++k) {
+    const int v = vindex(k);
+    if (v >= total) break;
+    set_block(v);
+    if (k0 >= N) continue;  // a short sequence of a variable-length batch: no keys here
+    // Prologue: K/V rows (unless staged), tiles qt0 and qt0+1 loading; once all have
+    // landed, K/V into AGPRs and tile qt0's rows.
+    if (k > 0) __builtin_amdgcn_s_barrier();  // the last block's tiles are no longer read
+    else issue_kv(head, k0, N);
+    issue_q(qt0, Q0, G0, L0, E0);
+    if (qt0 + 1 < nqt) issue_q(qt0 + 1, Q1, G1, L1, E1);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+    kv_inflight = false;
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_kv();
+    zero_acc();
+    zero_pd();
+    kcur = k;
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) prefetch_rows(Q0, G0, kk);
-  int qt = qt0;
-  for (; qt + 3 < nqt; qt += 4) {  // whole rotations: no conditional steps in the body
-    step(qt, Q3, G3, L0, E0, Q1, G1, Q2, G2, L2s, E2);
-    step(qt + 1, Q0, G0, L1, E1, Q2, G2, Q3, G3, L3, E3);
-    step(qt + 2, Q1, G1, L2s, E2, Q3, G3, Q0, G0, L0, E0);
-    step(qt + 3, Q2, G2, L3, E3, Q0, G0, Q1, G1, L1, E1);
-  }
-  if (qt < nqt) step(qt, Q3, G3, L0, E0, Q1, G1, Q2, G2, L2s, E2);
-  if (qt + 1 < nqt) step(qt + 1, Q0, G0, L1, E1, Q2, G2, Q3, G3, L3, E3);
-  if (qt + 2 < nqt) step(qt + 2, Q1, G1, L2s, E2, Q3, G3, Q0, G0, L0, E0);
-  // dV/dK of the last tile (buffer set (nqt - 1 - qt0) % 4, intact: no later loads)
-  {
-    const int last = (nqt - 1 - qt0) % 4;
-    const __bf16* Qp = last == 0 ? Q0 : last == 1 ? Q1 : last == 2 ? Q2 : Q3;
-    const __bf16* Gp = last == 0 ? G0 : last == 1 ? G1 : last == 2 ? G2 : G3;
+    for (int kk = 0; kk < NKK; ++kk) prefetch_rows(Q0, G0, kk);
+    int qt = qt0;
+    for (; qt + 3 < nqt; qt += 4) {  // whole rotations: no conditional steps in the body
+      step(qt, Q3, G3, L0, E0, Q1, G1, Q2, G2, L2s, E2);
+      step(qt + 1, Q0, G0, L1, E1, Q2, G2, Q3, G3, L3, E3);
+      step(qt + 2, Q1, G1, L2s, E2, Q3, G3, Q0, G0, L0, E0);
+      step(qt + 3, Q2, G2, L3, E3, Q0, G0, Q1, G1, L1, E1);
+    }
+    // Stage the next block's rows after step nqt - 3, which issues the last tile load (or
+    // after the first step if there is none), so that they are the newest loads in flight;
+    // past the first step's barrier every wave has read this block's K/V.
+    const bool stage = vindex(k + 1) < total;
+    auto stage_next = [&]() {
+      issue_kv_next();
+      kv_inflight = true;
+    };
+    if (stage && qt > qt0 && qt >= nqt - 2) stage_next();
+    if (qt < nqt) step(qt, Q3, G3, L0, E0, Q1, G1, Q2, G2, L2s, E2);
+    if (stage && !kv_inflight) stage_next();
+    if (qt + 1 < nqt) step(qt + 1, Q0, G0, L1, E1, Q2, G2, Q3, G3, L3, E3);
+    if (qt + 2 < nqt) step(qt + 2, Q1, G1, L2s, E2, Q3, G3, Q0, G0, L0, E0);
+    // dV/dK of the last tile (buffer set (nqt - 1 - qt0) % 4, intact: no later loads)
+    {
+      const int last = (nqt - 1 - qt0) % 4;
+      const __bf16* Qp = last == 0 ? Q0 : last == 1 ? Q1 : last == 2 ? Q2 : Q3;
+      const __bf16* Gp = last == 0 ? G0 : last == 1 ? G1 : last == 2 ? G2 : G3;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const bf16x8_t bg = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
-        const bf16x8_t bq = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8_t bg = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
+          const bf16x8_t bq = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
 #pragma unroll
-        for (int b = 0; b < KB; ++b) {
-          mma_a(dv[b][dt], pa[b][j], bg);
-          mma_a(dk[b][dt], da[b][j], bq);
+          for (int b = 0; b < KB; ++b) {
+            mma_a(dv[b][dt], pa[b][j], bg);
+            mma_a(dk[b][dt], da[b][j], bq);
+          }
         }
-      }
-  }
-  // No direct load or prefetch read may still be in flight when the wave ends.
-  __builtin_amdgcn_s_waitcnt(0x0070);
+    }
+    // The last step's reads of the next tile's rows (stale: never used) are back.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
 
-  // MFMA results in AGPRs: 16 wait states before v_accvgpr_read may take them.
-  asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dk[0][0]), "+a"(dv[0][0]));
+    // MFMA results in AGPRs: 16 wait states before v_accvgpr_read may take them.
+    asm volatile("s_nop 7\n\ts_nop 7" : "+a"(dk[0][0]), "+a"(dv[0][0]));
 #pragma unroll
-  for (int b = 0; b < KB; ++b)
+    for (int b = 0; b < KB; ++b)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dk[b][dt]), "+a"(dv[b][dt]));
-  // dK (scaled) and dV: lane = dim column, register = key row.
+      for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dk[b][dt]), "+a"(dv[b][dt]));
+    // dK (scaled) and dV: lane = dim column, register = key row.
 #pragma unroll
-  for (int b = 0; b < KB; ++b)
+    for (int b = 0; b < KB; ++b)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kw + 32 * b + crow(g, r);
-        if (key < N) {
-          const size_t off = head + (size_t)k0 * D + ((key - k0) * D + dt * 32 + l32);
-          dK[off] = (__bf16)(dk[b][dt][r] * scale);
-          dV[off] = (__bf16)dv[b][dt][r];
+        for (int r = 0; r < 16; ++r) {
+          const int key = kw + 32 * b + crow(g, r);
+          if (key < N) {
+            const size_t off = head + (size_t)k0 * D + ((key - k0) * D + dt * 32 + l32);
+            dK[off] = (__bf16)(dk[b][dt][r] * scale);
+            dV[off] = (__bf16)dv[b][dt][r];
+          }
         }
-      }
+  }
+  // No direct load may still be in flight when the wave ends.
+  __builtin_amdgcn_s_waitcnt(0x0070);
 }
 
 template <int D, bool GEN>
 static hipError_t launch_bwd_bf16_d(const BwdArgs& a) {
   using C = BwdFast<D>;
   const int nkb = (a.N + C::BKV - 1) / C::BKV;
-  const long long grid = (long long)a.B * a.H * nkb;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const long long total = (long long)a.B * a.H * nkb;
+  if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // One wave per SIMD fills a CU: dense calls run one persistent workgroup per CU (a
+  // multiple of 8, for the rounds' XCD order), each taking its blocks in turn and staging
+  // the next one's K/V while it finishes the current one.  Variable-length and windowed
+  // calls, whose blocks differ irregularly in cost, keep one workgroup per block.
+  long long grid = total;
+  if (!GEN) {
+    const int ncu = compute_units();
+    if (ncu >= 8 && total > ncu) grid = ncu - ncu % 8;
+  }
   launch_begin();
   hipLaunchKernelGGL((bwd_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dk,
-                     (__bf16*)a.dv, a.N, a.Npad, a.scale, a.causal, nkb,
+                     (__bf16*)a.dv, a.N, a.Npad, a.scale, a.causal, nkb, (int)total,
                      SeqMap{a.cu_seqlens, a.B, a.T}, a.window);
   return hipGetLastError();
 }

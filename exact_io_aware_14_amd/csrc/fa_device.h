@@ -129,6 +129,25 @@ __device__ __forceinline__ void dma16(const void* base, unsigned voff, const voi
   asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
+// A wave-uniform pointer as a 64-bit scalar register pair.
+__device__ __forceinline__ unsigned long long sgpr_ptr(const void* p) {
+  const unsigned long long t = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)t);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(t >> 32));
+  return ((unsigned long long)hi << 32) | lo;
+}
+// dma16 from a base already in scalar registers (sgpr_ptr).  A vector-ALU write of the
+// base (v_readfirstlane) needs five wait states before a load reads it; callers that form
+// the base right before their loads separate the two with sgpr_wait.
+__device__ __forceinline__ void dma16_s(unsigned long long sbase, unsigned voff, const void* lds_wave) {
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds_addr(lds_wave));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+// Five wait states after the scalar registers of a and b were last written.
+__device__ __forceinline__ void sgpr_wait(unsigned long long a, unsigned long long b) {
+  asm volatile("s_nop 4" ::"s"(a), "s"(b));
+}
+
 // Block id -> logical work id.  Consecutive workgroup ids are spread round robin
 // over the 8 XCDs (each with its own L2); the remap hands each XCD a contiguous
 // range of logical ids, so the tiles of one (batch, head) share that XCD's L2.

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <atomic>
+
 namespace fa {
 
 enum { kBF16 = 0, kFP32 = 1 };
@@ -12,6 +14,20 @@ enum { kBF16 = 0, kFP32 = 1 };
 // calls left in this thread's error slot out of it, so that the hipGetLastError()
 // after the launch reports only what the launch itself caused.
 inline void launch_begin() { (void)hipGetLastError(); }
+
+// Compute units of the current device, queried once per device (0 if the query fails:
+// callers then launch one workgroup per block).
+inline int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 0) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
 
 // Per-head row padding of the backward's D and lse workspace vectors: every
 // backward query tile (32 rows) reads whole padded vectors.
