@@ -27,6 +27,17 @@ def _assembly(src: str, out_dir: str) -> str:
     return out
 
 
+def _sgprs(operand: str) -> set:
+    """SGPR names an operand covers: "s8" -> {s8}, "s[8:9]" -> {s8, s9}."""
+    m = re.fullmatch(r"s(\d+)", operand)
+    if m:
+        return {operand}
+    m = re.fullmatch(r"s\[(\d+):(\d+)\]", operand)
+    if m:
+        return {"s%d" % r for r in range(int(m.group(1)), int(m.group(2)) + 1)}
+    return set()
+
+
 def _hazards(lines):
     """(line, instruction) of every load whose base SGPRs are written in the five wait
     states before it."""
@@ -46,7 +57,7 @@ def _hazards(lines):
             if parts[0] == "s_nop":
                 ws += int(parts[1], 0) + 1
                 continue
-            if parts[0].startswith("v_") and len(parts) > 1 and parts[1] in base:  # vector-ALU write
+            if parts[0].startswith("v_") and len(parts) > 1 and _sgprs(parts[1]) & base:  # vector-ALU write
                 bad.append((i, t))
                 break
             ws += 1
@@ -58,6 +69,9 @@ def test_hazard_scan_finds_a_planted_case():
              "\tglobal_load_lds_dwordx4 v1, s[8:9]"]
     assert len(_hazards(lines)) == 1
     assert _hazards(["\tv_readfirstlane_b32 s8, v2", "\ts_nop 4", "\tglobal_load_lds_dwordx4 v1, s[8:9]"]) == []
+    # a vector instruction with a register-pair destination (a compare) counts as well
+    assert len(_hazards(["\tv_cmp_gt_i32_e64 s[8:9], v1, v2", "\tglobal_load_lds_dwordx4 v1, s[8:9]"])) == 1
+    assert _hazards(["\tv_readfirstlane_b32 s7, v2", "\tglobal_load_lds_dwordx4 v1, s[8:9]"]) == []
     # scalar-ALU writes of the base need no wait states
     assert _hazards(["\ts_add_u32 s8, s2, s4", "\ts_addc_u32 s9, s3, 0", "\tglobal_load_lds_dwordx4 v1, s[8:9]"]) == []
 
