@@ -127,6 +127,33 @@ def test_varlen_equal_lengths_bitwise_dense(dev, causal):
         assert torch.equal(a, pk(b))
 
 
+@pytest.mark.parametrize("B,H,N,d,causal", [(4, 32, 4096, 128, True), (4, 16, 2048, 64, True),
+                                             (1, 13, 2560, 128, False), (1, 13, 2560, 128, True)])
+def test_persistent_dkdv_equals_one_block_per_workgroup(dev, B, H, N, d, causal):
+    """Dense calls with more key blocks than CUs run the dK/dV pass as one looping
+    workgroup per CU (blocks in rounds, every second round reversed within an XCD, each
+    block's K/V staged by the block before it); variable-length calls run the same kernel
+    with one workgroup per block.  With equal lengths both must give every element bit
+    for bit.  Shapes: the long causal layer (4096 blocks, 16 rounds), the training-step
+    shape at d = 64 (two key blocks per wave), and 260 blocks (not a multiple of 8: a
+    partial last round, plain block order)."""
+    say(f"[persistent dK/dV] B={B} H={H} N={N} d={d} causal={causal}")
+    w = Workload("persist", B, H, N, d, causal, "bf16", True, seed=11)
+    x = make_inputs(w)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, w.scale, causal)
+    g = fa.bwd(q, k, v, o, do, lse, w.scale, causal)
+    pk = lambda t: t.permute(1, 0, 2, 3).reshape(H, B * N, d).contiguous()
+    cu = torch.arange(0, (B + 1) * N, N, dtype=torch.int32, device=dev)
+    ov, lv = fa.fwd_ex(pk(q), pk(k), pk(v), w.scale, causal, cu_seqlens=cu, max_seqlen=N)
+    gv = fa.bwd_ex(pk(q), pk(k), pk(v), ov, pk(do), lv, w.scale, causal, cu_seqlens=cu, max_seqlen=N)
+    torch.cuda.synchronize()
+    assert torch.equal(ov, pk(o))
+    for name, a, b in zip(("dQ", "dK", "dV"), gv, g):
+        assert torch.equal(a, pk(b)), name
+    assert all(bool(torch.isfinite(t).all()) for t in g)
+
+
 def test_window_long_full_size(dev):
     """The long-context shape with a 4096-key window, two whole heads against the oracle."""
     w, window = WINDOW_WORKLOADS["window_long"]
