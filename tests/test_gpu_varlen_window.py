@@ -128,15 +128,17 @@ def test_varlen_equal_lengths_bitwise_dense(dev, causal):
 
 
 @pytest.mark.parametrize("B,H,N,d,causal", [(4, 32, 4096, 128, True), (4, 16, 2048, 64, True),
-                                             (1, 13, 2560, 128, False), (1, 13, 2560, 128, True)])
+                                             (1, 13, 2560, 128, False), (1, 13, 2560, 128, True),
+                                             (8, 64, 100, 128, True), (8, 40, 200, 64, False)])
 def test_persistent_dkdv_equals_one_block_per_workgroup(dev, B, H, N, d, causal):
     """Dense calls with more key blocks than CUs run the dK/dV pass as one looping
     workgroup per CU (blocks in rounds, every second round reversed within an XCD, each
     block's K/V staged by the block before it); variable-length calls run the same kernel
     with one workgroup per block.  With equal lengths both must give every element bit
     for bit.  Shapes: the long causal layer (4096 blocks, 16 rounds), the training-step
-    shape at d = 64 (two key blocks per wave), and 260 blocks (not a multiple of 8: a
-    partial last round, plain block order)."""
+    shape at d = 64 (two key blocks per wave), 260 blocks (not a multiple of 8: a partial
+    last round, plain block order), and sequences shorter than one key block (every block
+    a tail block: staged rows past the end clamped, their keys masked)."""
     say(f"[persistent dK/dV] B={B} H={H} N={N} d={d} causal={causal}")
     w = Workload("persist", B, H, N, d, causal, "bf16", True, seed=11)
     x = make_inputs(w)
