@@ -28,14 +28,18 @@ fa_status check_sizes(int B, int H, int N, int d, float scale, int causal, int d
 }
 
 // Workspace: D [B*H*Npad] | lse*log2(e) [B*H*Npad] (both dtypes), then for fp32
-// only a dQ accumulator [B*H*Npad*d]; all float32, each region 256-byte aligned.
+// only a dQ accumulator [B*H*Npad*d] (float32), then the int32 block plan of the
+// variable-length / windowed dK/dV pass; each region 256-byte aligned.
 size_t vec_bytes(int B, int H, int N) {
   return round_up((size_t)B * H * fa::pad_rows(N) * sizeof(float), kWsAlign);
 }
-size_t ws_bytes(int B, int H, int N, int d, int dtype) {
+size_t acc_bytes(int B, int H, int N, int d, int dtype) {
   const size_t prows = (size_t)B * H * fa::pad_rows(N);
-  const size_t acc = dtype == FA_DTYPE_FP32 ? round_up(prows * d * sizeof(float), kWsAlign) : 0;
-  return 2 * vec_bytes(B, H, N) + acc;
+  return dtype == FA_DTYPE_FP32 ? round_up(prows * d * sizeof(float), kWsAlign) : 0;
+}
+size_t ws_bytes(int B, int H, int N, int d, int dtype) {
+  const size_t plan = round_up(fa::plan_ints(B, H, N) * sizeof(int), kWsAlign);
+  return 2 * vec_bytes(B, H, N) + acc_bytes(B, H, N, d, dtype) + plan;
 }
 
 // Extra checks of the variable-length / window calls (see fa.h).
@@ -131,7 +135,8 @@ static fa::BwdArgs bwd_args(const void* q, const void* k, const void* v, const v
   float* Dvec = (float*)workspace;
   float* L2 = (float*)((char*)workspace + vb);
   float* dqacc = dtype == FA_DTYPE_FP32 ? (float*)((char*)workspace + 2 * vb) : nullptr;
-  return fa::BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, Dvec, L2, dqacc,
+  int* plan = (int*)((char*)workspace + 2 * vb + acc_bytes(B, H, N, d, dtype));
+  return fa::BwdArgs{q, k, v, o, dout, lse, dq, dk, dv, Dvec, L2, dqacc, plan,
                      B, H, N, d, fa::pad_rows(N), scale, causal, dtype, stream};
 }
 

@@ -77,12 +77,126 @@ __device__ __forceinline__ bf16x8_t tr_pair(const __bf16* lo, const __bf16* hi) 
   return r;
 }
 
+// Query tiles qt0 .. nqt-1 that see a block of keys k0 .. k0+BKV-1 of a sequence of n
+// rows: causal rows before k0 see none of its keys, and in a window rows past the last
+// key's band see none.
+template <int BKV, int BQ>
+__device__ __forceinline__ void key_block_tiles(int n, int k0, int causal, int window, int& qt0, int& nqt) {
+  nqt = (n + BQ - 1) / BQ;
+  qt0 = causal ? k0 / BQ : 0;
+  if (window > 0) nqt = min(nqt, (k0 + BKV - 1 + window - 1) / BQ + 1);
+}
+
+// The plan of a variable-length or windowed dK/dV launch, built on the device from the
+// sequence table by one workgroup right before it.  Blocks of keys (id = unit * nkb + key
+// block) that hold keys are split into 8 contiguous id ranges of about equal cost (steps
+// plus a fixed cost per block), one per XCD, so that a unit's blocks share an L2; each
+// range is sorted by steps, most first, so that the workgroups of an XCD, taking its
+// list in rounds, end close together.  Layout: plan[x] = start of XCD x's list,
+// plan[8] = end of the last, ids from plan[kPlanHead] on.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBins = 1024;  // steps classes of the sort (steps >> shift)
+constexpr int kPlanFix = 3;      // a block's prologue and stores, in steps
+static_assert(kPlanHead >= 9, "plan header");
+
+template <int BKV, int BQ>
+__global__ __launch_bounds__(kPlanThreads) void bwd_plan_kernel(SeqMap sm, int Nmax, int causal, int window,
+                                                               int nkb, int total, int* __restrict__ plan) {
+  __shared__ long long part[kPlanThreads];
+  __shared__ int bins[8 * kPlanBins];
+  const int t = threadIdx.x;
+  // Inclusive prefix sum over the workgroup's threads.
+  auto scan = [&](long long v) -> long long {
+    part[t] = v;
+    __syncthreads();
+    for (int off = 1; off < kPlanThreads; off <<= 1) {
+      const long long a = t >= off ? part[t - off] : 0;
+      __syncthreads();
+      part[t] += a;
+      __syncthreads();
+    }
+    const long long r = part[t];
+    __syncthreads();
+    return r;
+  };
+  // Each thread walks a contiguous run of ids; a run spans few units, whose length it keeps.
+  const int seg = total / kPlanThreads + (total % kPlanThreads != 0);
+  const int i0 = min(t * seg, total), i1 = min(i0 + seg, total);
+  int unit = -1, n = 0;
+  auto steps = [&](int id) -> int {  // 0: no keys in this block
+    const int u = id / nkb, kb = id - u * nkb;
+    if (u != unit) {
+      int base;
+      seq_rows(sm, u, Nmax, base, n);
+      unit = u;
+    }
+    if (kb * BKV >= n) return 0;
+    int qt0, nqt;
+    key_block_tiles<BKV, BQ>(n, kb * BKV, causal, window, qt0, nqt);
+    return nqt - qt0;
+  };
+  int shift = 0;
+  while ((((Nmax + BQ - 1) / BQ) >> shift) >= kPlanBins) ++shift;
+  auto bin_of = [&](int st) { return kPlanBins - 1 - min(st >> shift, kPlanBins - 1); };
+
+  for (int i = t; i < 8 * kPlanBins; i += kPlanThreads) bins[i] = 0;
+  long long mine = 0;
+  for (int id = i0; id < i1; ++id) {
+    const int st = steps(id);
+    if (st > 0) mine += st + kPlanFix;
+  }
+  const long long incl = scan(mine);
+  const long long ctot = part[kPlanThreads - 1];
+  __syncthreads();
+  // XCD of a block: the eighth of the total cost that holds the block's midpoint.
+  auto xcd_of = [&](long long p, int cost) -> int {
+    return (int)min(7LL, 8 * (2 * p + cost) / (2 * ctot));
+  };
+  long long p = incl - mine;
+  for (int id = i0; id < i1; ++id) {
+    const int st = steps(id);
+    if (st > 0) {
+      atomicAdd(&bins[xcd_of(p, st + kPlanFix) * kPlanBins + bin_of(st)], 1);
+      p += st + kPlanFix;
+    }
+  }
+  __syncthreads();
+  // Counts -> list positions: XCD-major, and within an XCD the most steps first.
+  constexpr int PER = 8 * kPlanBins / kPlanThreads;
+  int cnt[PER], sum = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    cnt[j] = bins[t * PER + j];
+    sum += cnt[j];
+  }
+  const long long pos_incl = scan(sum);
+  int run = (int)(pos_incl - sum);
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    bins[t * PER + j] = run;
+    run += cnt[j];
+  }
+  __syncthreads();
+  if (t < 8) plan[t] = bins[t * kPlanBins];
+  if (t == kPlanThreads - 1) plan[8] = run;
+  __syncthreads();
+  p = incl - mine;
+  for (int id = i0; id < i1; ++id) {
+    const int st = steps(id);
+    if (st > 0) {
+      const int at = atomicAdd(&bins[xcd_of(p, st + kPlanFix) * kPlanBins + bin_of(st)], 1);
+      plan[kPlanHead + at] = id;
+      p += st + kPlanFix;
+    }
+  }
+}
+
 template <int D, bool GEN>
 __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ L2, const float* __restrict__ Dvec,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int Nmax, int Npad, float scale, int causal,
-    int nkb, int total, SeqMap sm_arg, int window_arg) {
+    int nkb, int total, SeqMap sm_arg, int window_arg, const int* __restrict__ plan) {
   // GEN = false: dense tensors, no window; the general code folds away.
   const int window = GEN ? window_arg : 0;
   const SeqMap sm{GEN ? sm_arg.cu : nullptr, sm_arg.B, sm_arg.T};
@@ -125,25 +239,43 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
   constexpr int KB = C::KB;
-  // Logical blocks (id: unit and key block, heaviest first when causal) are taken in
-  // rounds k = 0, 1, ... of nwg = gridDim.x at a time.  A launch of one workgroup per block
-  // runs one round.  A persistent launch (fewer workgroups, each looping) walks every
-  // second round backwards within its XCD (nwg a multiple of 8), so a workgroup's blocks
-  // alternate between the heavy and the light end of a round; blocks stay on the XCD
-  // whose L2 holds their unit's rows, as with one workgroup per block.
+  // Dense calls: logical blocks (id: unit and key block, heaviest first when causal) are
+  // taken in rounds k = 0, 1, ... of nwg = gridDim.x at a time.  A launch of one workgroup
+  // per block runs one round.  A persistent launch (fewer workgroups, each looping) walks
+  // every second round backwards within its XCD (nwg a multiple of 8), so a workgroup's
+  // blocks alternate between the heavy and the light end of a round; blocks stay on the
+  // XCD whose L2 holds their unit's rows, as with one workgroup per block.
+  // General calls (always persistent, nwg a multiple of 8): workgroup wi runs on XCD
+  // wi % 8 and takes that XCD's list in the plan (most steps first) in the same rounds.
   const int nwg = gridDim.x;
+  int lbeg = 0, lend = 0;
+  if constexpr (GEN) {
+    lbeg = plan[blockIdx.x & 7];
+    lend = plan[(blockIdx.x & 7) + 1];
+  }
   auto vindex = [&](int k) -> int {
     const int wi = blockIdx.x;
+    if constexpr (GEN) {
+      const int nx = nwg >> 3, li = wi >> 3;
+      return k * nx + ((k & 1) ? nx - 1 - li : li);
+    }
     if ((nwg & 7) != 0 || !(k & 1)) return k * nwg + wi;
     return k * nwg + (nwg - 8 - (wi & ~7)) + (wi & 7);
   };
+  auto has = [&](int v) -> bool { return GEN ? lbeg + v < lend : v < total; };
   auto block_of = [&](int v, int& bh_, int& kb_) {
+    if constexpr (GEN) {
+      const int id = plan[kPlanHead + lbeg + v];
+      bh_ = id / nkb;
+      kb_ = id - bh_ * nkb;
+      return;
+    }
     const int id = xcd_remap(v, total);
     bh_ = id / nkb;
     kb_ = id - bh_ * nkb;
     if (causal) {  // the first key blocks see the most query tiles: heaviest first
       int t;
-      heavy_first(id, nkb, total / nkb, GEN ? 1 : heavy_group(Nmax, D), bh_, t);
+      heavy_first(id, nkb, total / nkb, heavy_group(Nmax, D), bh_, t);
       kb_ = nkb - 1 - t;
     }
   };
@@ -158,11 +290,9 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     hpad = (size_t)bh * Npad;
     k0 = kb * C::BKV;
     kw = k0 + w * 32 * KB;
-    // query tiles of this sequence (its padded rows hold lse = +inf: P = 0 there) ...
-    nqt = (N + C::BQ - 1) / C::BQ;
-    qt0 = causal ? k0 / C::BQ : 0;  // ... earlier rows see none of these keys
-    if (window > 0)  // ... nor do rows past the last key's band
-      nqt = min(nqt, (k0 + C::BKV - 1 + window - 1) / C::BQ + 1);
+    // query tiles of this sequence that see these keys (its padded rows hold lse = +inf:
+    // P = 0 there)
+    key_block_tiles<C::BKV, C::BQ>(N, k0, causal, window, qt0, nqt);
   };
 
   // --- direct-load source offsets ------------------------------------------------
@@ -490,17 +620,28 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     reinterpret_cast<v16b*>(Q3)[i] = v16b{0, 0, 0, 0};
     reinterpret_cast<v16b*>(G3)[i] = v16b{0, 0, 0, 0};
   }
-  // Every block after a workgroup's first found its K/V rows staged by the one before it:
-  // dense blocks are never empty, and other calls run one round.
+  // A block after a workgroup's first finds its K/V rows staged by the one before it
+  // (kv_inflight).  Neither dense blocks nor planned ones are ever empty; should a planned
+  // one be, its staged rows are waited for and the next block loads its own.
   for (int k = 0;; ++k) {
     const int v = vindex(k);
-    if (v >= total) break;
+    if (!has(v)) break;
     set_block(v);
-    if (k0 >= N) continue;  // a short sequence of a variable-length batch: no keys here
     // Prologue: K/V rows (unless staged), tiles qt0 and qt0+1 loading; once all have
     // landed, K/V into AGPRs and tile qt0's rows.
-    if (k > 0) __builtin_amdgcn_s_barrier();  // the last block's tiles are no longer read
-    else issue_kv(head, k0, N);
+    if constexpr (GEN) {
+      if (k0 >= N) {  // no keys here
+        if (kv_inflight) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        kv_inflight = false;
+        continue;
+      }
+      if (k > 0) __builtin_amdgcn_s_barrier();  // the last block's tiles are no longer read
+      if (!kv_inflight) issue_kv(head, k0, N);
+    } else {
+      if (k0 >= N) continue;  // (never taken; kept for the compiler's register allocation)
+      if (k > 0) __builtin_amdgcn_s_barrier();  // as above
+      else issue_kv(head, k0, N);
+    }
     issue_q(qt0, Q0, G0, L0, E0);
     if (qt0 + 1 < nqt) issue_q(qt0 + 1, Q1, G1, L1, E1);
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
@@ -523,7 +664,7 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     // Stage the next block's rows after step nqt - 3, which issues the last tile load (or
     // after the first step if there is none), so that they are the newest loads in flight;
     // past the first step's barrier every wave has read this block's K/V.
-    const bool stage = vindex(k + 1) < total;
+    const bool stage = has(vindex(k + 1));
     auto stage_next = [&]() {
       issue_kv_next();
       kv_inflight = true;
@@ -585,21 +726,29 @@ static hipError_t launch_bwd_bf16_d(const BwdArgs& a) {
   const int nkb = (a.N + C::BKV - 1) / C::BKV;
   const long long total = (long long)a.B * a.H * nkb;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // One wave per SIMD fills a CU: dense calls run one persistent workgroup per CU (a
+  // One wave per SIMD fills a CU: the pass runs one persistent workgroup per CU (a
   // multiple of 8, for the rounds' XCD order), each taking its blocks in turn and staging
   // the next one's K/V while it finishes the current one.  Variable-length and windowed
-  // calls, whose blocks differ irregularly in cost, keep one workgroup per block.
+  // calls, whose blocks differ irregularly in cost, take them from a plan sorted by cost.
+  const int ncu = compute_units();
   long long grid = total;
-  if (!GEN) {
-    const int ncu = compute_units();
-    if (ncu >= 8 && total > ncu) grid = ncu - ncu % 8;
-  }
+  const SeqMap sm{a.cu_seqlens, a.B, a.T};
   launch_begin();
+  if (!GEN) {
+    if (ncu >= 8 && total > ncu) grid = ncu - ncu % 8;
+  } else {
+    // The plan first (one workgroup), then one workgroup per CU, a multiple of 8.
+    hipLaunchKernelGGL((bwd_plan_kernel<C::BKV, C::BQ>), dim3(1), dim3(kPlanThreads), 0,
+                       (hipStream_t)a.stream, sm, a.N, a.causal, a.window, nkb, (int)total, a.plan);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    grid = ncu >= 8 ? ncu - ncu % 8 : 8;
+  }
   hipLaunchKernelGGL((bwd_bf16_kernel<D, GEN>), dim3((unsigned)grid), dim3(C::NT), 0,
                      (hipStream_t)a.stream, (const __bf16*)a.q, (const __bf16*)a.k,
                      (const __bf16*)a.v, (const __bf16*)a.dout, a.L2, a.Dvec, (__bf16*)a.dk,
-                     (__bf16*)a.dv, a.N, a.Npad, a.scale, a.causal, nkb, (int)total,
-                     SeqMap{a.cu_seqlens, a.B, a.T}, a.window);
+                     (__bf16*)a.dv, a.N, a.Npad, a.scale, a.causal, nkb, (int)total, sm,
+                     a.window, GEN ? (const int*)a.plan : nullptr);
   return hipGetLastError();
 }
 

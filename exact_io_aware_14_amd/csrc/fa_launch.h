@@ -34,6 +34,15 @@ inline int compute_units() {
 constexpr int kRowPad = 32;
 inline int pad_rows(int N) { return (N + kRowPad - 1) / kRowPad * kRowPad; }
 
+// The block plan of a variable-length or windowed dK/dV launch (workspace, int32): a
+// header of kPlanHead values, then one id per block of keys, at most one per 128 keys of
+// every (batch, head) unit.
+constexpr int kPlanHead = 16;
+constexpr int kPlanKeys = 128;
+inline size_t plan_ints(int B, int H, int N) {
+  return kPlanHead + (size_t)B * H * ((N + kPlanKeys - 1) / kPlanKeys);
+}
+
 // Dense calls: cu_seqlens = null, N the sequence length.  Variable-length calls:
 // cu_seqlens = B+1 device boundaries, tensors packed [H, T, d], N the longest length.
 // window > 0: causal band, query i sees key j iff i - window < j <= i.
@@ -57,6 +66,7 @@ struct BwdArgs {
   float* Dvec;   // [B*H*Npad] workspace: D_i = dO_i . O_i (0 on padding rows)
   float* L2;     // [B*H*Npad] workspace: lse_i * log2(e) (+inf on padding rows)
   float* dqacc;  // [B*H*Npad*d] workspace float32 dQ accumulator (fp32 path only; null for bf16)
+  int* plan;     // [plan_ints(B, H, N)] workspace: block plan of general bf16 dK/dV launches
   int B, H, N, d;
   int Npad;      // N rounded up to kRowPad
   float scale;

@@ -84,9 +84,10 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  int dtype, void* stream);
 
 /* Bytes of device workspace fa_bwd needs: two float32 vectors of B*H*Npad values
- * (Npad = N rounded up to a multiple of 32: D_i and lse_i * log2(e)), and for
- * FA_DTYPE_FP32 also a float32 dQ accumulator of [B, H, Npad, d]; each region
- * 256-byte aligned.  0 for invalid sizes. */
+ * (Npad = N rounded up to a multiple of 32: D_i and lse_i * log2(e)), for
+ * FA_DTYPE_FP32 also a float32 dQ accumulator of [B, H, Npad, d], then an int32 block
+ * plan of 16 + B*H*ceil(N/128) values (used by the variable-length and windowed bf16
+ * calls of fa_bwd_ex); each region 256-byte aligned.  0 for invalid sizes. */
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d, int dtype);
 
 /* Backward pass.
@@ -245,8 +246,9 @@ fa_status fa_merge(const float* o_part, const float* lse_part, void* o, float* l
  * until the process ends; its address is looked up once per device, on the first
  * call there.  The call allocates and frees nothing.
  *   - It fits iff fa_bwd_workspace_bytes(B, H, N, d, dtype) <= FA_NOALLOC_SCRATCH_BYTES
- *     (bf16: B*H*ceil32(N) <= 4M rows; fp32: B*H*ceil32(N)*(8 + 4d) bytes <= 32 MiB);
- *     a larger call returns FA_ERR_TOO_LARGE before anything is enqueued.
+ *     (about 8 + 1/32 bytes per padded row for bf16, 8 + 4d + 1/32 for fp32, so bf16
+ *     fits up to about 4.1M rows B*H*ceil32(N)); a larger call returns
+ *     FA_ERR_TOO_LARGE before anything is enqueued.
  *   - Every call on one GPU uses that GPU's one array: calls that overlap in time on one
  *     GPU (different streams, threads or processes' shared contexts) race and give
  *     undefined results; serialise them, e.g. on one stream.  Nothing a previous call

@@ -77,8 +77,9 @@ def test_bwd_check_codes_and_workspace():
     ws = L.fa_bwd_workspace_bytes(1, 2, 100, 64, 0)
     padded = 2 * 128  # N = 100 padded to a multiple of 32 per head
     rnd = lambda x: (x + 255) // 256 * 256
-    assert ws == 2 * rnd(padded * 4)  # bf16: D and lse vectors only
-    assert L.fa_bwd_workspace_bytes(1, 2, 100, 64, 1) == 2 * rnd(padded * 4) + rnd(padded * 64 * 4)
+    plan = rnd(4 * (16 + 2 * 1))  # block plan: header + one id per 128 keys of each head
+    assert ws == 2 * rnd(padded * 4) + plan  # bf16: D and lse vectors, plan
+    assert L.fa_bwd_workspace_bytes(1, 2, 100, 64, 1) == 2 * rnd(padded * 4) + rnd(padded * 64 * 4) + plan
     assert L.fa_bwd_workspace_bytes(1, 2, 100, 96, 0) == 0
     assert bwd_check(wsb=ws) == fa.FA_OK
     assert bwd_check(wsb=ws - 1) == fa.FA_ERR_INVALID_ARG
@@ -104,7 +105,8 @@ def test_noalloc_size_limit_is_checked_on_the_host():
     assert "FA_NOALLOC_SCRATCH_BYTES (32u << 20)" in open(HEADER).read()
     B, H, N, d = 64, 64, 1056, 64  # bf16: 2 x 4.3M padded rows of 4 bytes
     assert L.fa_bwd_workspace_bytes(B, H, N, d, 0) > limit
-    assert L.fa_bwd_workspace_bytes(64, 64, 1024, 64, 0) <= limit  # exactly 32 MiB fits
+    assert L.fa_bwd_workspace_bytes(64, 64, 1024, 64, 0) > limit  # 32 MiB of vectors + plan
+    assert L.fa_bwd_workspace_bytes(64, 63, 1024, 64, 0) <= limit
     args = lambda B, H, N, d, dt: (P, P, P, P, P, P, P, P, P, B, H, N, d, 0.125, 1, dt, None)
     assert L.fa_bwd_noalloc(*args(B, H, N, d, 0)) == fa.FA_ERR_TOO_LARGE
     # fp32 adds a [B, H, Npad, d] accumulator: 4 x 32 x 1024 rows x 520 bytes > 32 MiB

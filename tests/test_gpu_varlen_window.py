@@ -11,7 +11,8 @@ import torch
 
 from exact_io_aware_14_amd import fa
 from exact_io_aware_14_amd.inputs import (VARLEN_WORKLOADS, WINDOW_WORKLOADS, VarlenWorkload,
-                                          Workload, make_inputs, make_varlen_inputs, to_f64)
+                                          Workload, make_inputs, make_varlen_inputs, to_f64,
+                                          varlen_lengths)
 from oracle import attention_bwd, attention_fwd
 from oracle.varlen import varlen_bwd, varlen_fwd, window_mask
 from parity import check_fwd, check_grad, f64
@@ -134,8 +135,8 @@ def test_persistent_dkdv_equals_one_block_per_workgroup(dev, B, H, N, d, causal)
     """Dense calls with more key blocks than CUs run the dK/dV pass as one looping
     workgroup per CU (blocks in rounds, every second round reversed within an XCD, each
     block's K/V staged by the block before it); variable-length calls run the same kernel
-    with one workgroup per block.  With equal lengths both must give every element bit
-    for bit.  Shapes: the long causal layer (4096 blocks, 16 rounds), the training-step
+    over the blocks of their plan, in another order and grouping.  With equal lengths both
+    must give every element bit for bit.  Shapes: the long causal layer (4096 blocks, 16 rounds), the training-step
     shape at d = 64 (two key blocks per wave), 260 blocks (not a multiple of 8: a partial
     last round, plain block order), and sequences shorter than one key block (every block
     a tail block: staged rows past the end clamped, their keys masked)."""
@@ -154,6 +155,76 @@ def test_persistent_dkdv_equals_one_block_per_workgroup(dev, B, H, N, d, causal)
     for name, a, b in zip(("dQ", "dK", "dV"), gv, g):
         assert torch.equal(a, pk(b)), name
     assert all(bool(torch.isfinite(t).all()) for t in g)
+
+
+def plan_steps(n, kb, bkv, causal, window):
+    """Query tiles (32 rows) that see key block kb of a sequence of n rows."""
+    k0 = kb * bkv
+    nqt = -(-n // 32)
+    qt0 = k0 // 32 if causal else 0
+    if window > 0:
+        nqt = min(nqt, (k0 + bkv - 1 + window - 1) // 32 + 1)
+    return nqt - qt0
+
+
+@pytest.mark.parametrize("d,causal,window,lens,H", [
+    (128, True, 0, None, 16),                        # the varlen_mix lengths
+    (64, True, 0, None, 4),
+    (128, False, 0, [0, 5, 0, 129, 64, 300], 1),    # empty sequences; 6 units, 8 XCDs
+    (128, True, 50, [1000, 77, 3000], 3),
+    (64, True, 0, [1], 1),
+])
+def test_dkdv_plan_structure(dev, d, causal, window, lens, H):
+    """The dK/dV pass of a variable-length call takes its blocks of keys from a plan that
+    a one-workgroup kernel writes into the workspace right before it.  After a backward,
+    the plan must hold every block with keys exactly once and nothing else; each XCD's
+    list must cover a contiguous range of block ids, ranges in XCD order; each list must
+    run from the most query tiles to the fewest; and each XCD's cost (tiles + 3 per block)
+    must lie within one block's cost of an eighth of the total."""
+    if lens is None:
+        lens = [int(n) for n in varlen_lengths(VARLEN_WORKLOADS["varlen_mix"])]
+    say(f"[dK/dV plan] d={d} causal={causal} W={window} H={H} lens={lens[:6]}...")
+    B = len(lens)
+    w = VarlenWorkload("plan", B, 1, 1, H, d, causal, "bf16", seed=5)
+    x = make_varlen_inputs(w, lengths=lens)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    nmax = max(1, x["max_len"])
+    args = dict(scale=w.scale, causal=causal, window=window, cu_seqlens=x["cu"].to(dev), max_seqlen=nmax)
+    o, lse = fa.fwd_ex(q, k, v, **args)
+    nb = fa.workspace_bytes(B, H, nmax, d, q.dtype)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=dev)
+    fa.bwd_ex(q, k, v, o, do, lse, workspace=ws, **args)
+    torch.cuda.synchronize()
+    rnd = lambda n: (n + 255) // 256 * 256
+    off = 2 * rnd(B * H * (-(-nmax // 32) * 32) * 4)
+    plan = ws[off:].cpu().view(torch.int32).numpy()
+    bkv = 128 if d == 128 else 256
+    nkb = -(-nmax // bkv)
+    want = {}
+    for u in range(B * H):
+        n = lens[u % B]
+        for kb in range(-(-n // bkv)):
+            want[u * nkb + kb] = plan_steps(n, kb, bkv, causal, window)
+    heads, count = plan[:9], int(plan[8])
+    assert heads[0] == 0 and all(heads[i] <= heads[i + 1] for i in range(8)), heads
+    ids = plan[16:16 + count]
+    assert count == len(want) and sorted(ids.tolist()) == sorted(want), "plan != blocks with keys"
+    shift = 0
+    while (-(-nmax // 32) >> shift) >= 1024:
+        shift += 1
+    lists = [ids[heads[x]:heads[x + 1]].tolist() for x in range(8)]
+    last = -1
+    for lst in lists:
+        if not lst:
+            continue
+        assert min(lst) > last, "XCD ranges out of order or overlapping"
+        last = max(lst)
+        cls = [min(want[i] >> shift, 1023) for i in lst]
+        assert all(a >= b for a, b in zip(cls, cls[1:])), "list not sorted by tiles"
+    cost = {i: s + 3 for i, s in want.items()}
+    tot, big = sum(cost.values()), max(cost.values())
+    for lst in lists:
+        assert abs(sum(cost[i] for i in lst) - tot / 8) <= big, "XCD costs unbalanced"
 
 
 def test_window_long_full_size(dev):
