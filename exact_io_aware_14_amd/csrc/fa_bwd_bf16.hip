@@ -64,6 +64,20 @@ __device__ __forceinline__ int bswz(int r) {
   return D == 128 ? 4 * (r & 3) + ((r >> 2) & 3) : 4 * ((r >> 1) & 1) + ((r >> 2) & 3);
 }
 
+// Swizzle of the epilogue's [column][key] transpose (4-key chunks XOR-ed by a function
+// of the column): conflict-free on 64 banks both for the 8-byte writes in the accumulator
+// layout (32 consecutive columns, one chunk) and for the transposing reads (4 columns x 4
+// chunks per 16-lane group, two groups 8 columns apart per half-wave).
+template <int D>
+__device__ __forceinline__ int epi_swz(int col) {
+  if (D == 128) {  // 4 columns per 256-byte bank row: swap bits 1 and 2 of col / 4
+    const int x = (col >> 2) & 7;
+    return (x & 1) | (((x >> 1) & 1) << 2) | (((x >> 2) & 1) << 1);
+  }
+  const int x = (col >> 1) & 15;  // 2 columns per bank row: bits 0,1,2,3 -> 2,0,3,1
+  return ((x & 1) << 2) | ((x >> 1) & 1) | (((x >> 2) & 1) << 3) | (((x >> 3) & 1) << 1);
+}
+
 __device__ __forceinline__ bf16x8_t tr_pair(const __bf16* lo, const __bf16* hi) {
   const i16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)lo);
   const i16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)hi);
@@ -679,12 +693,25 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
       const int last = (nqt - 1 - qt0) % 4;
       const __bf16* Qp = last == 0 ? Q0 : last == 1 ? Q1 : last == 2 ? Q2 : Q3;
       const __bf16* Gp = last == 0 ? G0 : last == 1 ? G1 : last == 2 ? G2 : G3;
+      // The transposed-read offsets formed afresh (as trq): nothing the steps keep in
+      // registers needs to live on to here.
+      unsigned ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      int trf[2][NDT];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int row = 8 * h + 4 * ((int)ln >> 5) + (((int)ln >> 2) & 3);
+          const int col = dt * 32 + 16 * (((int)ln >> 4) & 1) + 4 * ((int)ln & 3);
+          trf[h][dt] = row * D + ((((col >> 3) ^ bswz<D>(row))) << 3) + (col & 7);
+        }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8_t bg = tr_pair(Gp + j * 16 * D + trq[0][dt], Gp + j * 16 * D + trq[1][dt]);
-          const bf16x8_t bq = tr_pair(Qp + j * 16 * D + trq[0][dt], Qp + j * 16 * D + trq[1][dt]);
+          const bf16x8_t bg = tr_pair(Gp + j * 16 * D + trf[0][dt], Gp + j * 16 * D + trf[1][dt]);
+          const bf16x8_t bq = tr_pair(Qp + j * 16 * D + trf[0][dt], Qp + j * 16 * D + trf[1][dt]);
 #pragma unroll
           for (int b = 0; b < KB; ++b) {
             mma_a(dv[b][dt], pa[b][j], bg);
@@ -701,20 +728,55 @@ __global__ __launch_bounds__(256) void bwd_bf16_kernel(
     for (int b = 0; b < KB; ++b)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) asm volatile("" : "+a"(dk[b][dt]), "+a"(dv[b][dt]));
-    // dK (scaled) and dV: lane = dim column, register = key row.
+    // dK (scaled) and dV, one tensor at a time, transposed through this wave's query-tile
+    // set (free now: once every wave has passed the barrier below, all have done their
+    // last products, and the next block loads its tiles only after its own barrier).
+    // Lane (g, c) holds column c of key rows crow(g, r); rows r = 4i .. 4i+3 are four
+    // consecutive keys and go to LDS as one 8-byte write in a [column][key] layout.
+    // Transposing reads of that layout give each lane 4 consecutive columns of one key, two
+    // reads 8, which leave with one 16-byte store: 16 stores per lane instead of 128.
+    __builtin_amdgcn_s_barrier();
+    {
+      unsigned ln;  // read afresh: nothing below is formed before the barrier
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      constexpr int KW = 32 * KB;   // keys per wave
+      constexpr int NKH = KW / 16;  // 16-key groups per wave
+      __bf16* const reg = w == 0 ? S0 : w == 1 ? S1 : w == 2 ? S2 : S3;  // KW x D bf16 fit
+      static_assert(KW * D <= 2 * C::QTILE, "a wave's tile fits its set");
+      auto loff = [](int col, int kc) { return col * KW + 4 * (kc ^ epi_swz<D>(col)); };
+      const int lg = (int)ln >> 5, lc = (int)ln & 31;
+      const int q = (int)ln >> 4, e = ((int)ln >> 2) & 3, j = (int)ln & 3, i16 = (int)ln & 15;
+      auto put = [&](f32x16_t (&acc)[KB][NDT], float mul, __bf16* dst) {
 #pragma unroll
-    for (int b = 0; b < KB; ++b)
+        for (int b = 0; b < KB; ++b)
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt)
+          for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kw + 32 * b + crow(g, r);
+            for (int i = 0; i < 4; ++i) {
+              bf16x4_t x;
+#pragma unroll
+              for (int t = 0; t < 4; ++t) x[t] = (__bf16)(acc[b][dt][4 * i + t] * mul);
+              *reinterpret_cast<bf16x4_t*>(reg + loff(dt * 32 + lc, 8 * b + 2 * i + lg)) = x;
+            }
+        // lane (q, e, j) of read h fetches column 32cb + 8q + 4h + e, keys 16kh + 4j ..
+        // +3; lane (q, i) receives columns 32cb + 8q + 4h .. +3 of key 16kh + i.
+#pragma unroll
+        for (int s = 0; s < NKH * NDT; ++s) {
+          const int kh = s % NKH, cb = s / NKH;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(reg + loff(32 * cb + 8 * q + e, 4 * kh + j)));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(reg + loff(32 * cb + 8 * q + 4 + e, 4 * kh + j)));
+          const int key = kw + 16 * kh + i16;
           if (key < N) {
-            const size_t off = head + (size_t)k0 * D + ((key - k0) * D + dt * 32 + l32);
-            dK[off] = (__bf16)(dk[b][dt][r] * scale);
-            dV[off] = (__bf16)dv[b][dt][r];
+            const v16b val = __builtin_bit_cast(v16b, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            *reinterpret_cast<v16b*>(dst + head + (size_t)key * D + 32 * cb + 8 * q) = val;
           }
         }
+      };
+      put(dk, scale, dK);
+      put(dv, 1.0f, dV);
+    }
   }
   // No direct load may still be in flight when the wave ends.
   __builtin_amdgcn_s_waitcnt(0x0070);
