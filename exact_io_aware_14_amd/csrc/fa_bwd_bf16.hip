@@ -109,33 +109,46 @@ __device__ __forceinline__ void key_block_tiles(int n, int k0, int causal, int w
 // list in rounds, end close together.  Layout: plan[x] = start of XCD x's list,
 // plan[8] = end of the last, ids from plan[kPlanHead] on.
 constexpr int kPlanThreads = 1024;
-constexpr int kPlanBins = 1024;  // steps classes of the sort (steps >> shift)
-constexpr int kPlanFix = 3;      // a block's prologue and stores, in steps
+constexpr int kPlanBins = 1024;    // steps classes of the sort (steps >> shift)
+constexpr int kPlanFix = 3;        // a block's prologue and stores, in steps
+constexpr int kPlanCache = 16384;  // blocks whose steps are kept in LDS between the passes
 static_assert(kPlanHead >= 9, "plan header");
 
 template <int BKV, int BQ>
 __global__ __launch_bounds__(kPlanThreads) void bwd_plan_kernel(SeqMap sm, int Nmax, int causal, int window,
                                                                int nkb, int total, int* __restrict__ plan) {
-  __shared__ long long part[kPlanThreads];
+  constexpr int NWV = kPlanThreads / 64;
+  __shared__ long long wsum[NWV];
   __shared__ int bins[8 * kPlanBins];
-  const int t = threadIdx.x;
-  // Inclusive prefix sum over the workgroup's threads.
-  auto scan = [&](long long v) -> long long {
-    part[t] = v;
-    __syncthreads();
-    for (int off = 1; off < kPlanThreads; off <<= 1) {
-      const long long a = t >= off ? part[t - off] : 0;
-      __syncthreads();
-      part[t] += a;
-      __syncthreads();
+  __shared__ unsigned short cache[kPlanCache];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // Inclusive prefix sum over the workgroup's threads (within each wave by shuffles, then
+  // over the waves' sums); `all` receives the total.
+  auto scan = [&](long long v, long long& all) -> long long {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const long long a = __shfl_up(v, off, 64);
+      if (lane >= off) v += a;
     }
-    const long long r = part[t];
+    if (lane == 63) wsum[wv] = v;
     __syncthreads();
-    return r;
+    long long before = 0;
+    all = 0;
+#pragma unroll
+    for (int i = 0; i < NWV; ++i) {
+      const long long x = wsum[i];
+      before += i < wv ? x : 0;
+      all += x;
+    }
+    __syncthreads();  // wsum is free for the next scan
+    return v + before;
   };
   // Each thread walks a contiguous run of ids; a run spans few units, whose length it keeps.
+  // The first pass keeps each block's steps in LDS (when they fit) for the other two.
   const int seg = total / kPlanThreads + (total % kPlanThreads != 0);
   const int i0 = min(t * seg, total), i1 = min(i0 + seg, total);
+  const int smax = (Nmax + BQ - 1) / BQ;
+  const bool cached = total <= kPlanCache && smax < 65536;
   int unit = -1, n = 0;
   auto steps = [&](int id) -> int {  // 0: no keys in this block
     const int u = id / nkb, kb = id - u * nkb;
@@ -149,26 +162,29 @@ __global__ __launch_bounds__(kPlanThreads) void bwd_plan_kernel(SeqMap sm, int N
     key_block_tiles<BKV, BQ>(n, kb * BKV, causal, window, qt0, nqt);
     return nqt - qt0;
   };
+  auto steps_again = [&](int id) -> int { return cached ? (int)cache[id] : steps(id); };
   int shift = 0;
-  while ((((Nmax + BQ - 1) / BQ) >> shift) >= kPlanBins) ++shift;
+  while ((smax >> shift) >= kPlanBins) ++shift;
   auto bin_of = [&](int st) { return kPlanBins - 1 - min(st >> shift, kPlanBins - 1); };
 
   for (int i = t; i < 8 * kPlanBins; i += kPlanThreads) bins[i] = 0;
   long long mine = 0;
   for (int id = i0; id < i1; ++id) {
     const int st = steps(id);
+    if (cached) cache[id] = (unsigned short)st;
     if (st > 0) mine += st + kPlanFix;
   }
-  const long long incl = scan(mine);
-  const long long ctot = part[kPlanThreads - 1];
-  __syncthreads();
-  // XCD of a block: the eighth of the total cost that holds the block's midpoint.
+  long long ctot;
+  const long long incl = scan(mine, ctot);  // (its barriers also order the zeroed bins)
+  // XCD of a block: the eighth of the total cost that holds the block's midpoint (in
+  // double precision: the same rounding in both passes that use it, and no 64-bit division).
+  const double per = ctot > 0 ? 4.0 / (double)ctot : 0.0;
   auto xcd_of = [&](long long p, int cost) -> int {
-    return (int)min(7LL, 8 * (2 * p + cost) / (2 * ctot));
+    return min(7, (int)((double)(2 * p + cost) * per));
   };
   long long p = incl - mine;
   for (int id = i0; id < i1; ++id) {
-    const int st = steps(id);
+    const int st = steps_again(id);
     if (st > 0) {
       atomicAdd(&bins[xcd_of(p, st + kPlanFix) * kPlanBins + bin_of(st)], 1);
       p += st + kPlanFix;
@@ -183,8 +199,8 @@ __global__ __launch_bounds__(kPlanThreads) void bwd_plan_kernel(SeqMap sm, int N
     cnt[j] = bins[t * PER + j];
     sum += cnt[j];
   }
-  const long long pos_incl = scan(sum);
-  int run = (int)(pos_incl - sum);
+  long long count;
+  int run = (int)(scan(sum, count) - sum);
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     bins[t * PER + j] = run;
@@ -192,11 +208,11 @@ __global__ __launch_bounds__(kPlanThreads) void bwd_plan_kernel(SeqMap sm, int N
   }
   __syncthreads();
   if (t < 8) plan[t] = bins[t * kPlanBins];
-  if (t == kPlanThreads - 1) plan[8] = run;
+  if (t == 8) plan[8] = (int)count;
   __syncthreads();
   p = incl - mine;
   for (int id = i0; id < i1; ++id) {
-    const int st = steps(id);
+    const int st = steps_again(id);
     if (st > 0) {
       const int at = atomicAdd(&bins[xcd_of(p, st + kPlanFix) * kPlanBins + bin_of(st)], 1);
       plan[kPlanHead + at] = id;

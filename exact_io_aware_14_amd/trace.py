@@ -17,7 +17,8 @@ import re
 import statistics
 import sys
 
-LABELS = [("bwd_dq_bf16_kernel", "dQ pass"), ("bwd_bf16_kernel", "dK/dV pass"), ("fwd_bf16_kernel", "forward"),
+LABELS = [("bwd_dq_bf16_kernel", "dQ pass"), ("bwd_bf16_kernel", "dK/dV pass"), ("bwd_plan_kernel", "dK/dV plan"),
+          ("fwd_bf16_kernel", "forward"),
           ("bwd_pre_kernel", "bwd preprocess"), ("splitkv_partial_kernel", "split-KV partial"),
           ("splitkv_merge_kernel", "split-KV merge")]
 
