@@ -167,34 +167,13 @@ def plan_steps(n, kb, bkv, causal, window):
     return nqt - qt0
 
 
-@pytest.mark.parametrize("d,causal,window,lens,H", [
-    (128, True, 0, None, 16),                        # the varlen_mix lengths
-    (64, True, 0, None, 4),
-    (128, False, 0, [0, 5, 0, 129, 64, 300], 1),    # empty sequences; 6 units, 8 XCDs
-    (128, True, 50, [1000, 77, 3000], 3),
-    (64, True, 0, [1], 1),
-])
-def test_dkdv_plan_structure(dev, d, causal, window, lens, H):
-    """The dK/dV pass of a variable-length call takes its blocks of keys from a plan that
-    a one-workgroup kernel writes into the workspace right before it.  After a backward,
-    the plan must hold every block with keys exactly once and nothing else; each XCD's
-    list must cover a contiguous range of block ids, ranges in XCD order; each list must
-    run from the most query tiles to the fewest; and each XCD's cost (tiles + 3 per block)
-    must lie within one block's cost of an eighth of the total."""
-    if lens is None:
-        lens = [int(n) for n in varlen_lengths(VARLEN_WORKLOADS["varlen_mix"])]
-    say(f"[dK/dV plan] d={d} causal={causal} W={window} H={H} lens={lens[:6]}...")
+def check_plan(ws, lens, H, nmax, d, causal, window):
+    """The block plan the dK/dV pass left in the workspace: every block with keys exactly
+    once and nothing else; each XCD's list a contiguous range of block ids, ranges in XCD
+    order; each list from the most query tiles to the fewest (in the kernel's classes of
+    steps); each XCD's cost (tiles + 3 per block) within one block's cost of an eighth of
+    the total."""
     B = len(lens)
-    w = VarlenWorkload("plan", B, 1, 1, H, d, causal, "bf16", seed=5)
-    x = make_varlen_inputs(w, lengths=lens)
-    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
-    nmax = max(1, x["max_len"])
-    args = dict(scale=w.scale, causal=causal, window=window, cu_seqlens=x["cu"].to(dev), max_seqlen=nmax)
-    o, lse = fa.fwd_ex(q, k, v, **args)
-    nb = fa.workspace_bytes(B, H, nmax, d, q.dtype)
-    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=dev)
-    fa.bwd_ex(q, k, v, o, do, lse, workspace=ws, **args)
-    torch.cuda.synchronize()
     rnd = lambda n: (n + 255) // 256 * 256
     off = 2 * rnd(B * H * (-(-nmax // 32) * 32) * 4)
     plan = ws[off:].cpu().view(torch.int32).numpy()
@@ -225,6 +204,73 @@ def test_dkdv_plan_structure(dev, d, causal, window, lens, H):
     tot, big = sum(cost.values()), max(cost.values())
     for lst in lists:
         assert abs(sum(cost[i] for i in lst) - tot / 8) <= big, "XCD costs unbalanced"
+
+
+@pytest.mark.parametrize("d,causal,window,lens,H", [
+    (128, True, 0, None, 16),                        # the varlen_mix lengths
+    (64, True, 0, None, 4),
+    (128, False, 0, [0, 5, 0, 129, 64, 300], 1),    # empty sequences; 6 units, 8 XCDs
+    (128, True, 50, [1000, 77, 3000], 3),
+    (64, True, 0, [1], 1),
+])
+def test_dkdv_plan_structure(dev, d, causal, window, lens, H):
+    """The dK/dV pass of a variable-length call takes its blocks of keys from a plan that
+    a one-workgroup kernel writes into the workspace right before it (checked by
+    check_plan after a backward)."""
+    if lens is None:
+        lens = [int(n) for n in varlen_lengths(VARLEN_WORKLOADS["varlen_mix"])]
+    say(f"[dK/dV plan] d={d} causal={causal} W={window} H={H} lens={lens[:6]}...")
+    B = len(lens)
+    w = VarlenWorkload("plan", B, 1, 1, H, d, causal, "bf16", seed=5)
+    x = make_varlen_inputs(w, lengths=lens)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    nmax = max(1, x["max_len"])
+    args = dict(scale=w.scale, causal=causal, window=window, cu_seqlens=x["cu"].to(dev), max_seqlen=nmax)
+    o, lse = fa.fwd_ex(q, k, v, **args)
+    nb = fa.workspace_bytes(B, H, nmax, d, q.dtype)
+    ws = torch.full((nb,), 0xFF, dtype=torch.uint8, device=dev)
+    fa.bwd_ex(q, k, v, o, do, lse, workspace=ws, **args)
+    torch.cuda.synchronize()
+    check_plan(ws, lens, H, nmax, d, causal, window)
+
+
+@pytest.mark.parametrize("d,H,lens", [
+    (128, 8, "many"),     # 96 sequences: 24,576 block ids, past the plan's LDS cache of steps
+    (64, 2, [40000, 3]),  # a 40,000-token sequence: steps up to 1,250, classes of two steps
+])
+def test_dkdv_plan_at_scale_equals_dense(dev, d, H, lens):
+    """Larger plans: more block ids than the plan kernel keeps in LDS (it recomputes their
+    steps), and steps beyond its 1,024 sort classes.  Besides the plan's structure, every
+    sequence's dK and dV must equal, bit for bit, a dense backward of that sequence alone
+    (same blocks, same tiles, same summation order; only the schedule differs)."""
+    if lens == "many":
+        rng = np.random.default_rng(17)
+        lens = [int(n) for n in rng.integers(1, 4097, size=96)]
+        lens[0], lens[1] = 4096, 0
+    B, causal = len(lens), True
+    say(f"[dK/dV plan at scale] d={d} H={H} B={B} max={max(lens)}")
+    w = VarlenWorkload("plan_scale", B, 1, 1, H, d, causal, "bf16", seed=19)
+    x = make_varlen_inputs(w, lengths=lens)
+    q, k, v, do = (x[n].to(dev) for n in ("q", "k", "v", "do"))
+    nmax = max(lens)
+    cu = x["cu"]
+    args = dict(scale=w.scale, causal=causal, cu_seqlens=cu.to(dev), max_seqlen=nmax)
+    o, lse = fa.fwd_ex(q, k, v, **args)
+    ws = torch.full((fa.workspace_bytes(B, H, nmax, d, q.dtype),), 0xFF, dtype=torch.uint8, device=dev)
+    dq, dk, dv = fa.bwd_ex(q, k, v, o, do, lse, workspace=ws, **args)
+    torch.cuda.synchronize()
+    check_plan(ws, lens, H, nmax, d, causal, 0)
+    for b in sorted({0, B - 1, int(np.argmin([n if n else 1 << 30 for n in lens])), B // 2}):
+        n = lens[b]
+        if n == 0:
+            continue
+        sl = lambda t: t[:, int(cu[b]):int(cu[b + 1])].unsqueeze(0).contiguous()
+        od, ld = fa.fwd(sl(q), sl(k), sl(v), w.scale, causal)
+        g = fa.bwd(sl(q), sl(k), sl(v), od, sl(do), ld, w.scale, causal)
+        torch.cuda.synchronize()
+        assert torch.equal(od, sl(o)), f"O of sequence {b}"
+        for name, a, ref in zip(("dQ", "dK", "dV"), (dq, dk, dv), g):
+            assert torch.equal(sl(a), ref), f"{name} of sequence {b} (length {n})"
 
 
 def test_window_long_full_size(dev):
