@@ -38,14 +38,21 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 // softmax in the tile loop); far inside fp32 and bf16 range.
 constexpr float kWeightBound = 1048576.0f;  // 2^20
 
+// d = 128: tiles of 32 keys, so that a wave fits 168 registers and three waves share each
+// SIMD (three workgroups per CU): one K operand read in flight ahead of the products, V
+// operands read where the products need them.  d = 64: tiles of 64 keys, three waves per
+// SIMD already; four K reads ahead, and the V operands of a tile's first 16 keys read before
+// its softmax.
 template <int D>
 struct FwdFast {
   static constexpr int NW = 4;             // waves per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int BR = 32 * NW;       // query rows per workgroup
-  static constexpr int BC = 64;            // keys per K/V tile
+  static constexpr int BC = D == 128 ? 32 : 64;  // keys per K/V tile
   static constexpr int NKS = BC / 32;      // 32-key halves of a tile
-  static constexpr int OCC = 2;            // waves per SIMD the registers are sized for
+  static constexpr int OCC = D == 128 ? 3 : 2;   // waves per SIMD the registers are sized for
+  static constexpr int AHEAD = D == 128 ? 1 : 4; // K operand reads in flight (d-steps)
+  static constexpr bool EARLY_V = D == 64;       // first V operands read before the softmax
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int TILE = BC * D;      // elements per K (or V) tile
   static constexpr int LOADS = BC * CPR / 64 / NW;  // direct loads per wave per tile
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     // K operand reads run AHEAD d-steps in front of the products that use them, so
     // the LDS round trips overlap each other and the products instead of alternating
     // with them (at most 15 LDS reads may be outstanding for a counted wait).
-    constexpr int AHEAD = NKK < 4 ? NKK : 4;
+    constexpr int AHEAD = C::AHEAD < NKK ? C::AHEAD : NKK;
     const bool need_mask = (k0 + C::BC > N) || (causal && k0 + C::BC - 1 > qw) ||
                            (window > 0 && k0 <= qw + 31 - window);
     f32x16_t s[NKS];
@@ -251,12 +258,16 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
       }
       return a;
     };
-    // The operands of the tile's first 16 keys are read before the softmax, so that their
-    // LDS latency passes under it and the PV products can start on its last weight.
-    bf16x8_t vfirst[NDT];
+    // At d = 64 the operands of the tile's first 16 keys are read before the softmax, so
+    // that their LDS latency passes under it and the PV products can start on its last
+    // weight (at d = 128 the third wave of each SIMD hides that latency, and the registers
+    // are needed for it).
+    bf16x8_t vfirst[C::EARLY_V ? NDT : 1];
+    if constexpr (C::EARLY_V) {
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) vfirst[dt] = read_v(0, 0, dt);
-    __builtin_amdgcn_sched_barrier(0);
+      for (int dt = 0; dt < NDT; ++dt) vfirst[dt] = read_v(0, 0, dt);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // Online softmax against the lazily moved reference mref: p = 2^(s*c - mref*c).
     // The theorem's exactness needs only one common reference for l and o~, and the
@@ -343,7 +354,9 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
         lsum_bf = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb, pb, 6, 7), ones2, lsum_bf, false);
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8_t a = (ks == 0 && j == 0) ? vfirst[dt] : read_v(ks, j, dt);
+          bf16x8_t a;
+          if constexpr (C::EARLY_V) a = (ks == 0 && j == 0) ? vfirst[dt] : read_v(ks, j, dt);
+          else a = read_v(ks, j, dt);
           oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, oacc[dt], 0, 0, 0);
         }
       }
