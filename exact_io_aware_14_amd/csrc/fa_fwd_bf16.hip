@@ -53,6 +53,11 @@ struct FwdFast {
   static constexpr int OCC = D == 128 ? 3 : 2;   // waves per SIMD the registers are sized for
   static constexpr int AHEAD = D == 128 ? 1 : 4; // K operand reads in flight (d-steps)
   static constexpr bool EARLY_V = D == 64;       // first V operands read before the softmax
+  // Wave priorities (s_setprio) of the S products and of the PV products; the softmax runs
+  // at 0.  PRIO_GEN: whether the general (windowed / variable-length) kernel sets them too.
+  static constexpr int PRIO_S = 1;
+  static constexpr int PRIO_PV = D == 128 ? 2 : 1;
+  static constexpr bool PRIO_GEN = D == 128;
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int TILE = BC * D;      // elements per K (or V) tile
   static constexpr int LOADS = BC * CPR / 64 / NW;  // direct loads per wave per tile
@@ -213,11 +218,12 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
           ka[kk][ks] = *reinterpret_cast<const bf16x8_t*>(
               Kb + k_rd + (ks * 2 * CPR * 16 + kk * 2 * 16) * 8);
       };
-      // Wave priority 1 while the wave issues its products, 0 during its softmax: when
-      // both waves of a SIMD are ready, the one feeding the matrix cores goes first, and
-      // the other's vector work fills in, which pushes the two into opposite phases.  (The
-      // general variant measured slightly slower with it and keeps a flat priority.)
-      if constexpr (!GEN) __builtin_amdgcn_s_setprio(1);
+      // Wave priority raised while the wave issues its products, 0 during its softmax: when
+      // several waves of a SIMD are ready, the ones feeding the matrix cores go first, and
+      // the others' vector work fills in, which pushes them into different phases.  At
+      // d = 128 (three waves a SIMD) the PV products rank above the S products, and the
+      // general kernel uses the same order; at d = 64 its flat priority measured faster.
+      if constexpr (!GEN || C::PRIO_GEN) __builtin_amdgcn_s_setprio(C::PRIO_S);
 #pragma unroll
       for (int kk = 0; kk < AHEAD; ++kk) read_k(kk);
 #pragma unroll
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
           s[ks] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk][ks], qop[kk], s[ks], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (!GEN) __builtin_amdgcn_s_setprio(0);
+      if constexpr (!GEN || C::PRIO_GEN) __builtin_amdgcn_s_setprio(0);
       if (need_mask) {  // keys past the end, above the diagonal or below the window
         const int hi = causal ? min(myq, N - 1) : N - 1;
         const int lo = window > 0 ? myq - window + 1 : 0;
@@ -340,7 +346,7 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
     lsum += t;
 
     // O^T += V^T P^T
-    if constexpr (!GEN) __builtin_amdgcn_s_setprio(1);
+    if constexpr (!GEN || C::PRIO_GEN) __builtin_amdgcn_s_setprio(C::PRIO_PV);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
