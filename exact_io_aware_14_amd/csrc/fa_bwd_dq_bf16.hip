@@ -201,6 +201,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         ak[kk] = *reinterpret_cast<const bf16x8_t*>(Kb + ks * 32 * D + nat[kk]);
         av[kk] = *reinterpret_cast<const bf16x8_t*>(Vb + ks * 32 * D + nat[kk]);
       };
+      // Dense calls at d = 128: wave priority 1 for the S and dP products, 2 for the dQ
+      // products, 0 for the softmax between them, so that of two ready waves on a SIMD the
+      // one feeding the matrix cores issues first (measured: the windowed kernel and d = 64
+      // are faster without).
+      constexpr bool kPrio = !GEN && D == 128;
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < AHEAD; ++kk) read_kv(kk);
 #pragma unroll
@@ -210,6 +216,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         __builtin_amdgcn_sched_barrier(0);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[kk], qop[kk], s, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[kk], gop[kk], dp, 0, 0, 0);
+      }
+      if constexpr (kPrio) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(0);
       }
       // K^T operands of this half's dQ product (transposed reads).  At d = 64 they are
       // read here, so their LDS round trips run under the softmax below; at d = 128 the
@@ -249,6 +259,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
         dp[r] = p * (dp[r] - dval);
       }
       // dQ^T += K^T dS^T over this half's 32 keys (2 steps of 16, c-layout key order).
+      if constexpr (kPrio) __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         bf16x8_t b;
