@@ -39,7 +39,7 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 constexpr float kWeightBound = 1048576.0f;  // 2^20
 
 // d = 128: tiles of 32 keys, so that a wave fits 168 registers and three waves share each
-// SIMD (three workgroups per CU): one K operand read in flight ahead of the products, V
+// SIMD (three workgroups per CU): two K operand reads in flight ahead of the products, V
 // operands read where the products need them.  d = 64: tiles of 64 keys, three waves per
 // SIMD already; four K reads ahead, and the V operands of a tile's first 16 keys read before
 // its softmax.
@@ -51,12 +51,12 @@ struct FwdFast {
   static constexpr int BC = D == 128 ? 32 : 64;  // keys per K/V tile
   static constexpr int NKS = BC / 32;      // 32-key halves of a tile
   static constexpr int OCC = D == 128 ? 3 : 2;   // waves per SIMD the registers are sized for
-  static constexpr int AHEAD = D == 128 ? 1 : 4; // K operand reads in flight (d-steps)
+  static constexpr int AHEAD = D == 128 ? 2 : 4; // K operand reads in flight (d-steps)
   static constexpr bool EARLY_V = D == 64;       // first V operands read before the softmax
   // Wave priorities (s_setprio) of the S products and of the PV products; the softmax runs
   // at 0.  PRIO_GEN: whether the general (windowed / variable-length) kernel sets them too.
   static constexpr int PRIO_S = 1;
-  static constexpr int PRIO_PV = D == 128 ? 2 : 1;
+  static constexpr int PRIO_PV = 2;
   static constexpr bool PRIO_GEN = D == 128;
   static constexpr int CPR = D / 8;        // 16-byte chunks per row
   static constexpr int TILE = BC * D;      // elements per K (or V) tile
@@ -221,8 +221,8 @@ __global__ __launch_bounds__(256, FwdFast<D>::OCC) void fwd_bf16_kernel(
       // Wave priority raised while the wave issues its products, 0 during its softmax: when
       // several waves of a SIMD are ready, the ones feeding the matrix cores go first, and
       // the others' vector work fills in, which pushes them into different phases.  At
-      // d = 128 (three waves a SIMD) the PV products rank above the S products, and the
-      // general kernel uses the same order; at d = 64 its flat priority measured faster.
+      // The PV products rank above the S products; at d = 128 (three waves a SIMD) the
+      // general kernel uses the same order, at d = 64 its flat priority measured faster.
       if constexpr (!GEN || C::PRIO_GEN) __builtin_amdgcn_s_setprio(C::PRIO_S);
 #pragma unroll
       for (int kk = 0; kk < AHEAD; ++kk) read_k(kk);
