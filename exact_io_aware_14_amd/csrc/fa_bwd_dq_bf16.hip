@@ -72,7 +72,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16_kernel(
   const int g = lane >> 5, l32 = lane & 31;
   const int id = xcd_remap(blockIdx.x, gridDim.x);
   int bh = id / nqb, qb = id - bh * nqb;
-  if (causal) heavy_first(id, nqb, gridDim.x / nqb, GEN ? 1 : heavy_group(Nmax, D), bh, qb);  // longest first
+  // Longest first, over groups of twice heavy_group's L2-sized count of units (capped at 8):
+  // measured -0.3 to -0.6 % against heavy_group's own count on the long causal layer, at
+  // N = 16384 and on the training step.
+  if (causal) heavy_first(id, nqb, gridDim.x / nqb, GEN ? 1 : min(8, 2 * heavy_group(Nmax, D)), bh, qb);
   int base, N;  // first row and length of this (batch, head)
   seq_rows(sm, bh, Nmax, base, N);
   const size_t head = (size_t)base * D;
