@@ -58,10 +58,11 @@ the L2's requests to the memory fabric, so K/V re-reads that miss the per-XCD 4 
 256 MB last-level cache count here too.  Algorithmic bytes: the tensors
 each kernel must read and write once (forward Q, K, V, O; dK/dV pass Q, K, V, dO, dK, dV; dQ pass,
 which forms D = dO . O itself, Q, K, V, dO, O, dQ), lse/D vectors left out.  A materialised score matrix would grow 16x from the
-first row to the last; the ratio staying flat is the linear traffic of the tiled method
-("FlashAttention and online softmax", "HBM traffic").  At N = 16384 (B = 1) one head's K and V
-(8 MB together) alone exceed an XCD's 4 MB L2, and the re-reads show up as the 1.4-1.5x ratio.  Source hashes
-(forward, dK/dV pass, dQ pass): {hash}.
+first row to the last; the tiled method's traffic stays linear in N ("FlashAttention and online
+softmax", "HBM traffic").  From N = 1024 to 8192 the ratios stay within {lo:.2f}-{hi:.2f}x.  At
+N = 16384 (B = 1) one head's K and V (8 MB together) alone exceed an XCD's 4 MB L2, and the
+causal head groups of the forward and the dQ pass hold two heads: their K/V re-reads miss L2
+({big}).  Source hashes (forward, dK/dV pass, dQ pass): {hash}.
 
 """
 
@@ -191,7 +192,11 @@ def main(argv=None) -> int:
         table = sweep(args.sweep, cal["fetch_scale"], cal["write_scale"])
         with open(SWEEP_OUT, "w") as f:
             hashes = ", ".join(f"`{source_hash(k)}`" for k in ("fwd_kernel", "bwd_main_kernel", "bwd_dq_kernel"))
-            f.write(SWEEP_HEADER.format(hash=hashes, dir=args.dir.rstrip("/"), sweep=args.sweep.rstrip("/"))
+            cells = [c for c in (r.split("|") for r in table.splitlines()) if c[2].strip().isdigit()]
+            small = [float(c[6]) for c in cells if int(c[2]) < 16384]
+            big = ", ".join(f"{c[1].strip()} {float(c[6]):.2f}x" for c in cells if int(c[2]) == 16384)
+            f.write(SWEEP_HEADER.format(hash=hashes, dir=args.dir.rstrip("/"), sweep=args.sweep.rstrip("/"),
+                                        lo=min(small), hi=max(small), big=big)
                     + table + "\n")
         print(table)
         return 0
